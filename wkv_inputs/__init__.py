@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the RWKV-4 WKV time-mixing path.
+
+This module is shared by the tests, the benchmark and the checker, and it holds
+none of the recurrence's arithmetic: it only draws random arrays, rounds them
+to the I/O dtype, and evaluates the per-channel initialisation recipe for the
+decay and bonus parameters.
+
+Recipe (all workloads):
+  * generator: numpy PCG64 seeded with ``1000 + workload index`` unless a seed
+    is given; draws are fp64 and are rounded once (round-to-nearest-even) to
+    the I/O dtype, so both sides of every comparison consume identical values;
+  * decay:  time_decay_c = -5 + 8 * (c / (C-1)) ** 1.35,  w_c = -exp(time_decay_c)
+  * bonus:  u_c = 0.5 * (((c + 1) mod 3) - 1) + ln(0.3)
+    (the initialisation these workloads are specified with; the pages give no
+    trained parameters);
+  * a random prior state is (aa ~ N(0,1), bb = |N(0,1)|, pp ~ U(-5,5)) in fp32,
+    planar [3, B, C]; bb is a sum of positive weights, so its magnitude is drawn.
+
+The five named workloads follow the shapes of the RWKV-4 169m and 14B models
+(d_model 768 and 5120, 40 layers, 1K context) and a long-context case at
+hidden size 2048 (the RWKV-GLM card's width).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "WORKLOADS", "Workload", "decay_bonus", "forward_case", "timemix_case",
+    "step_layer", "prior_state", "workload_inputs", "rng_for",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    kind: str            # "forward" | "timemix" | "step"
+    B: int
+    T: int
+    C: int
+    in_dtype: str        # "f32" | "f16"
+    out_dtype: str
+    gated: bool = False
+    prior: bool = False
+    k_sigma: float = 1.0
+    layers: int = 1
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    0: Workload(0, "rwkv4-169m wkv forward B1 T1024 C768 fp32", "forward",
+                1, 1024, 768, "f32", "f32"),
+    1: Workload(1, "rwkv4-169m gated prefill B8 T1024 C768 f16, prior state", "forward",
+                8, 1024, 768, "f16", "f16", gated=True, prior=True),
+    2: Workload(2, "rwkv4-14b time-mix fused prefill B1 T1024 C5120 f16", "timemix",
+                1, 1024, 5120, "f16", "f16", gated=True),
+    3: Workload(3, "rwkv4-14b batched decode 40 layers B256 C5120 f16", "step",
+                256, 1, 5120, "f16", "f16", gated=True, prior=True, layers=40),
+    4: Workload(4, "long-sequence chunked scan B1 T65536 C2048 f16->f32", "forward",
+                1, 65536, 2048, "f16", "f32", k_sigma=math.sqrt(2.0)),
+}
+
+_NP = {"f32": np.float32, "f16": np.float16}
+
+
+def rng_for(index: int, seed: int | None = None, stream: int | None = None) -> np.random.Generator:
+    """PCG64 generator: seed 1000+index by default; `stream` selects an independent
+    sub-stream (used per decode layer)."""
+    s = (1000 + index) if seed is None else seed
+    if stream is None:
+        return np.random.Generator(np.random.PCG64(s))
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([s, stream])))
+
+
+def _normal(rng, shape, dtype, sigma=1.0, shift=0.0):
+    a = rng.standard_normal(shape)
+    if sigma != 1.0:
+        a *= sigma
+    if shift != 0.0:
+        a += shift
+    return a.astype(_NP[dtype])
+
+
+def decay_bonus(C: int):
+    """Per-channel (w, u) as fp32 arrays of length C (recipe in the module doc)."""
+    c = np.arange(C, dtype=np.float64)
+    frac = c / (C - 1) if C > 1 else np.zeros_like(c)
+    time_decay = -5.0 + 8.0 * frac ** 1.35
+    w = -np.exp(time_decay)
+    u = 0.5 * (((c + 1) % 3) - 1) + math.log(0.3)
+    return w.astype(np.float32), u.astype(np.float32)
+
+
+def prior_state(rng, B: int, C: int) -> np.ndarray:
+    """Random prior state, planar fp32 [3, B, C] = (aa, bb, pp)."""
+    aa = rng.standard_normal((B, C))
+    bb = np.abs(rng.standard_normal((B, C)))
+    pp = rng.uniform(-5.0, 5.0, (B, C))
+    return np.stack([aa, bb, pp]).astype(np.float32)
+
+
+def forward_case(B, T, C, *, seed, in_dtype="f32", out_dtype=None, gated=False,
+                 prior=False, k_sigma=1.0, k_shift=0.0, index=0):
+    """Inputs for rwkv4_wkv_forward.  Draw order: k, v, [r], [aa, bb, pp]."""
+    g = rng_for(index, seed)
+    w, u = decay_bonus(C)
+    k = _normal(g, (B, T, C), in_dtype, k_sigma, k_shift)
+    v = _normal(g, (B, T, C), in_dtype)
+    r = _normal(g, (B, T, C), in_dtype) if gated else None
+    st = prior_state(g, B, C) if prior else None
+    return dict(B=B, T=T, C=C, w=w, u=u, k=k, v=v, r=r, state_in=st,
+                in_dtype=in_dtype, out_dtype=out_dtype or in_dtype)
+
+
+def timemix_case(B, T, C, *, seed, in_dtype="f16", out_dtype=None, index=2, prior=False):
+    """Inputs for rwkv4_timemix_fused.
+    Draw order: x, x_prev, mix_k, mix_v, mix_r, k, v, [aa, bb, pp]."""
+    g = rng_for(index, seed)
+    w, u = decay_bonus(C)
+    x = _normal(g, (B, T, C), in_dtype)
+    x_prev = _normal(g, (B, C), in_dtype)
+    mix_k = g.uniform(0.0, 1.0, C).astype(np.float32)
+    mix_v = g.uniform(0.0, 1.0, C).astype(np.float32)
+    mix_r = g.uniform(0.0, 1.0, C).astype(np.float32)
+    k = _normal(g, (B, T, C), in_dtype)
+    v = _normal(g, (B, T, C), in_dtype)
+    st = prior_state(g, B, C) if prior else None
+    return dict(B=B, T=T, C=C, w=w, u=u, x=x, x_prev=x_prev, mix_k=mix_k, mix_v=mix_v,
+                mix_r=mix_r, k=k, v=v, state_in=st, in_dtype=in_dtype,
+                out_dtype=out_dtype or in_dtype)
+
+
+def step_layer(layer: int, B: int, C: int, *, seed=None, in_dtype="f16", index=3):
+    """One decode layer: k, v, r [B, C] and a random state [3, B, C].
+    Each layer draws from its own sub-stream (seed, layer) in the order k, v, r, aa, bb, pp."""
+    g = rng_for(index, seed, stream=layer)
+    w, u = decay_bonus(C)
+    k = _normal(g, (B, C), in_dtype)
+    v = _normal(g, (B, C), in_dtype)
+    r = _normal(g, (B, C), in_dtype)
+    st = prior_state(g, B, C)
+    return dict(B=B, C=C, w=w, u=u, k=k, v=v, r=r, state=st, in_dtype=in_dtype)
+
+
+def workload_inputs(index: int, seed: int | None = None, **shape):
+    """Inputs for a named workload; `shape` may override B, T, C for reduced cases."""
+    wl = WORKLOADS[index]
+    B = shape.get("B", wl.B)
+    T = shape.get("T", wl.T)
+    C = shape.get("C", wl.C)
+    s = (1000 + index) if seed is None else seed
+    if wl.kind == "forward":
+        return forward_case(B, T, C, seed=s, in_dtype=wl.in_dtype, out_dtype=wl.out_dtype,
+                            gated=wl.gated, prior=wl.prior, k_sigma=wl.k_sigma, index=index)
+    if wl.kind == "timemix":
+        return timemix_case(B, T, C, seed=s, in_dtype=wl.in_dtype, out_dtype=wl.out_dtype,
+                            index=index)
+    if wl.kind == "step":
+        layers = shape.get("layers", wl.layers)
+        return [step_layer(l, B, C, seed=s, in_dtype=wl.in_dtype, index=index)
+                for l in range(layers)]
+    raise ValueError(wl.kind)
