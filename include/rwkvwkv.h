@@ -1,0 +1,167 @@
+/*
+ * rwkvwkv.h -- C ABI of librwkvwkv, the RWKV-4 WKV time-mixing path for AMD MI355X (gfx950).
+ *
+ * The operation (the WKV operator of the RWKV paper, arXiv 2305.13048, which the
+ * "RWKV-4 14B" architecture page cites; the TR-2026-0009 port report describes it
+ * in its Abstract, Methods and Reproducibility sections as a per-channel
+ * numerator/denominator/max recurrence carried in fp32 with the max-trick,
+ * followed by the receptance gate, with a token shift that mixes the current and
+ * previous token):
+ *
+ *   per batch row b and channel c, with decay w_c (natural-log units, <= 0; the
+ *   caller passes w = -exp(time_decay)) and bonus u_c,
+ *
+ *     wkv_t = ( e^{t w} N0 + sum_{i<t} e^{(t-1-i) w + k_i} v_i + e^{u + k_t} v_t )
+ *           / ( e^{t w} D0 + sum_{i<t} e^{(t-1-i) w + k_i}     + e^{u + k_t}     )
+ *
+ *   where (N0, D0) = (aa e^pp, bb e^pp) is the prior state (zero when absent).
+ *   Gated output: y_t = wkv_t / (1 + e^{-r_t}).
+ *
+ * State.  The recurrent state is a caller-owned, first-class object (the ChatRWKV
+ * page, "The interesting bit" and Caveats: the caller tracks which text each
+ * state belongs to).  It is planar fp32 [3][B][C] = (aa, bb, pp): numerator and
+ * denominator scaled by e^{-pp}.  Triples are equivalence classes:
+ * (aa, bb, pp) and (aa e^d, bb e^d, pp - d) are the same state; the library
+ * returns some member of the class.  pp must be finite.  Pass state_in = NULL
+ * for the empty state (no history).
+ *
+ * Layout.  Activations are row-major [B][T][C] (channel fastest, contiguous).
+ * Per-channel parameters (w, u, mix_*) are fp32 [C].  All tensor pointers are
+ * DEVICE memory owned by the caller; the library never frees them and holds no
+ * pointer past the call (beyond stream ordering of the work it enqueued).
+ *
+ * Execution.  Every entry point only validates on the host and enqueues work on
+ * `stream` (NULL = the null stream); it never synchronises.  All validation
+ * happens before any work is enqueued, so an error return leaves every output
+ * untouched.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  Nothing throws across the ABI.
+ *
+ * Errors.  Functions return RWKV_OK (0) or a negative rwkv_status;
+ * rwkv_last_error() gives a thread-local message for the last failure.
+ *
+ * Sizes are int64; B, C >= 1 and T >= 0 (T = 0 copies the state).
+ * Pointers must be aligned to their element size; when C % 4 == 0 and every
+ * activation pointer is 8-byte (fp16) / 16-byte (fp32) aligned the kernels use
+ * vector loads, otherwise a per-element path.  Inputs are assumed finite
+ * (w may be -inf: full forgetting); NaN/Inf propagate unchecked.
+ */
+#ifndef RWKVWKV_H
+#define RWKVWKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RWKV_ABI_VERSION 1
+
+typedef enum rwkv_status {
+    RWKV_OK = 0,
+    RWKV_ERR_ARG = -1,    /* bad size, NULL required pointer, bad option, bad aliasing */
+    RWKV_ERR_DTYPE = -2,  /* unknown dtype */
+    RWKV_ERR_ALIGN = -3,  /* pointer not aligned to its element size */
+    RWKV_ERR_HIP = -4,    /* the HIP runtime reported an error while enqueuing */
+    RWKV_ERR_NOMEM = -5   /* the library-cached workspace could not be allocated */
+} rwkv_status;
+
+typedef enum rwkv_dtype { RWKV_F32 = 0, RWKV_F16 = 1 } rwkv_dtype;
+
+typedef enum rwkv_algo {
+    RWKV_ALGO_AUTO = 0,        /* pick by shape */
+    RWKV_ALGO_SEQUENTIAL = 1,  /* one lane per (b, 4 channels), loop over T (large B*C) */
+    RWKV_ALGO_CHUNKED = 2      /* chunked scan over T with a cross-workgroup look-back */
+} rwkv_algo;
+
+/*
+ * Options (all fields optional; pass NULL for: fp32 in and out, ungated, auto).
+ * `size` must be set to sizeof(rwkv4_opts) (forward compatibility).
+ */
+typedef struct rwkv4_opts {
+    uint32_t size;
+    int32_t in_dtype;        /* rwkv_dtype of k, v, r (and x, x_prev, x_last, xk/xv_out) */
+    int32_t out_dtype;       /* rwkv_dtype of y */
+    const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
+                                NULL = ungated (y = wkv).  Must be NULL for timemix. */
+    int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto,
+                                else a power of two in [64, 1024] */
+    int32_t algo;            /* rwkv_algo */
+    void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
+                                else device memory of workspace_bytes >= the size
+                                rwkv4_workspace_bytes() reports, zero-filled by the
+                                caller once before its first use, then reusable */
+    size_t workspace_bytes;
+} rwkv4_opts;
+
+/*
+ * WKV forward over a sequence (prefill).
+ *   B, T, C      batch rows, tokens, channels.
+ *   w, u         [C] fp32: decay (= -exp(time_decay), natural-log units) and bonus.
+ *   k, v         [B,T,C] in_dtype.
+ *   y            [B,T,C] out_dtype: wkv_t, or sigmoid(r_t) * wkv_t when opts->r is set.
+ *   state_in     [3,B,C] fp32 prior state, or NULL for the empty state.
+ *   state_out    [3,B,C] fp32 state after the T tokens, or NULL.  May equal
+ *                state_in exactly (in-place update); no other overlap is allowed.
+ * Concurrent calls on different streams that use the chunked scan must not share
+ * a workspace (pass opts->workspace).  The chunked scan is not capturable into a
+ * HIP graph (its workspace is stamped per launch from the host).
+ */
+rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C,
+                              const float *w, const float *u,
+                              const void *k, const void *v, void *y,
+                              const float *state_in, float *state_out,
+                              hipStream_t stream, const rwkv4_opts *opts);
+
+/*
+ * One decode token for B independent sequences (the T = 1 case of the forward,
+ * with the state read and written in place).
+ *   k, v         [B,C] in_dtype;  r [B,C] in_dtype or NULL (ungated).
+ *   y            [B,C] out_dtype.
+ *   state        [3,B,C] fp32, read and updated in place (required).
+ */
+rwkv_status rwkv4_wkv_step(int64_t B, int64_t C, const float *w, const float *u,
+                           const void *k, const void *v, const void *r, void *y,
+                           float *state, rwkv_dtype in_dtype, rwkv_dtype out_dtype,
+                           hipStream_t stream);
+
+/*
+ * Time-mix core with the token shift and the receptance gate fused around the WKV
+ * (the port report's "token-shift (mix current and previous token)" and
+ * "time-mix gating").  With xs_0 = x_prev (zeros if NULL) and xs_t = x_{t-1}:
+ *   xr = mix_r * x + (1 - mix_r) * xs   (fp32 math), receptance r := xr,
+ *   y  = sigmoid(xr) * wkv(k, v)         with k, v supplied by the caller
+ *                                        (its projections of xk, xv),
+ *   xk_out = mix_k * x + (1 - mix_k) * xs,  xv_out likewise (each optional),
+ *   x_last = x_{T-1} (the next call's x_prev; optional).
+ *   x, k, v, xk_out, xv_out [B,T,C] and x_prev, x_last [B,C] use opts->in_dtype;
+ *   y uses opts->out_dtype; mix_* [C] fp32.  State as in rwkv4_wkv_forward.
+ */
+rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C,
+                                const void *x, const void *x_prev, void *x_last,
+                                const float *mix_k, const float *mix_v, const float *mix_r,
+                                const void *k, const void *v,
+                                const float *w, const float *u,
+                                void *y, void *xk_out, void *xv_out,
+                                const float *state_in, float *state_out,
+                                hipStream_t stream, const rwkv4_opts *opts);
+
+/* Static text for a status code. */
+const char *rwkv_status_string(rwkv_status s);
+
+/* Thread-local message for the last non-OK return on this thread ("" if none). */
+const char *rwkv_last_error(void);
+
+/* Bytes of workspace the chunked scan needs for this shape (chunk_len 0 = auto). */
+size_t rwkv4_workspace_bytes(int64_t B, int64_t T, int64_t C, int32_t chunk_len);
+
+/* RWKV_ABI_VERSION of the loaded library. */
+int rwkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKVWKV_H */

@@ -1,0 +1,332 @@
+// rwkvwkv_abi.hip -- the C ABI of librwkvwkv: argument validation, algorithm choice,
+// workspace management and launch.  Every check runs on the host before anything is
+// enqueued, so an error return leaves all outputs untouched.
+
+#include "rwkvwkv.h"
+#include "wkv_internal.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+using namespace rwkvwkv;
+
+namespace {
+
+thread_local char g_err[512];
+
+rwkv_status fail(rwkv_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rwkv_status ok() {
+    g_err[0] = 0;
+    return RWKV_OK;
+}
+
+rwkv_status hip_fail(hipError_t e, const char *where) {
+    return fail(RWKV_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Library-cached chunked-scan workspace, one per device, grown on demand.
+struct DeviceWorkspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<DeviceWorkspace> g_ws;
+std::atomic<uint32_t> g_epoch{0};
+
+// Launch stamp in [1, 2^30 - 1]; a zero-filled workspace never matches it.
+uint32_t next_epoch() { return (g_epoch.fetch_add(1, std::memory_order_relaxed) % ((1u << 30) - 1u)) + 1u; }
+
+rwkv_status cached_workspace(size_t need, hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    DeviceWorkspace &w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // the old buffer may still be in use by enqueued work
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t nb = need < (1u << 20) ? (1u << 20) : need;
+        void *p = nullptr;
+        e = hipMalloc(&p, nb);
+        if (e != hipSuccess) return fail(RWKV_ERR_NOMEM, "workspace of %zu bytes: %s", nb, hipGetErrorString(e));
+        e = hipMemsetAsync(p, 0, nb, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemsetAsync(workspace)");
+        }
+        w.ptr = p;
+        w.bytes = nb;
+    }
+    *out = w.ptr;
+    return RWKV_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void *p, size_t pn, const void *q, size_t qn) {
+    if (!p || !q || !pn || !qn) return false;
+    const char *a = (const char *)p, *b = (const char *)q;
+    return a < b + qn && b < a + pn;
+}
+
+const int64_t kMaxElems = (int64_t)1 << 46;
+
+rwkv_status check_dtype(int32_t d, const char *what) {
+    if (d != RWKV_F32 && d != RWKV_F16) return fail(RWKV_ERR_DTYPE, "%s: unknown dtype %d", what, (int)d);
+    return RWKV_OK;
+}
+
+size_t esize(int32_t d) { return d == RWKV_F16 ? 2 : 4; }
+
+struct Resolved {
+    int32_t in_dtype = RWKV_F32, out_dtype = RWKV_F32;
+    const void *r = nullptr;
+    int32_t chunk_len = 0, algo = RWKV_ALGO_AUTO;
+    void *workspace = nullptr;
+    size_t workspace_bytes = 0;
+};
+
+rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
+    if (!o) return RWKV_OK;
+    if (o->size != sizeof(rwkv4_opts))
+        return fail(RWKV_ERR_ARG, "opts->size is %u, expected sizeof(rwkv4_opts) = %zu", o->size,
+                    sizeof(rwkv4_opts));
+    rwkv_status s;
+    if ((s = check_dtype(o->in_dtype, "opts->in_dtype")) != RWKV_OK) return s;
+    if ((s = check_dtype(o->out_dtype, "opts->out_dtype")) != RWKV_OK) return s;
+    if (o->algo < RWKV_ALGO_AUTO || o->algo > RWKV_ALGO_CHUNKED)
+        return fail(RWKV_ERR_ARG, "opts->algo %d is not a rwkv_algo", (int)o->algo);
+    if (o->chunk_len != 0) {
+        const int c = o->chunk_len;
+        if (c < kMinChunk || c > kMaxChunk || (c & (c - 1)) != 0)
+            return fail(RWKV_ERR_ARG, "opts->chunk_len %d: must be 0 or a power of two in [%d, %d]", c,
+                        kMinChunk, kMaxChunk);
+    }
+    if (o->workspace && !aligned(o->workspace, 256))
+        return fail(RWKV_ERR_ALIGN, "opts->workspace must be 256-byte aligned");
+    r->in_dtype = o->in_dtype;
+    r->out_dtype = o->out_dtype;
+    r->r = o->r;
+    r->chunk_len = o->chunk_len;
+    r->algo = o->algo;
+    r->workspace = o->workspace;
+    r->workspace_bytes = o->workspace_bytes;
+    return RWKV_OK;
+}
+
+// Shared tail of the forward and time-mix entry points: validation of the common
+// tensors, algorithm choice, workspace, launch.
+rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
+    const int64_t B = a.B, T = a.T, C = a.C;
+    if (B < 1 || C < 1 || T < 0) return fail(RWKV_ERR_ARG, "sizes must satisfy B >= 1, C >= 1, T >= 0 (got %lld, %lld, %lld)",
+                                              (long long)B, (long long)T, (long long)C);
+    if (B > kMaxElems / C || (T > 0 && B * C > kMaxElems / T))
+        return fail(RWKV_ERR_ARG, "B*T*C too large");
+    if (!a.w || !a.u) return fail(RWKV_ERR_ARG, "w and u are required");
+    if (T > 0 && (!a.k || !a.v || !a.y)) return fail(RWKV_ERR_ARG, "k, v and y are required when T > 0");
+    const size_t ei = esize(o.in_dtype), eo = esize(o.out_dtype);
+    const void *ins[] = {a.k, a.v, a.r, a.x, a.x_prev, a.xk_out, a.xv_out, a.x_last};
+    for (const void *p : ins)
+        if (p && !aligned(p, ei)) return fail(RWKV_ERR_ALIGN, "activation pointer %p not aligned to %zu bytes", p, ei);
+    if (a.y && !aligned(a.y, eo)) return fail(RWKV_ERR_ALIGN, "y not aligned to %zu bytes", eo);
+    const float *fl[] = {a.w, a.u, a.mix_k, a.mix_v, a.mix_r, a.state_in, a.state_out};
+    for (const float *p : fl)
+        if (p && !aligned(p, 4)) return fail(RWKV_ERR_ALIGN, "fp32 pointer %p not 4-byte aligned", (const void *)p);
+    const size_t sbytes = (size_t)(3 * B * C) * 4;
+    if (a.state_out && a.state_in != a.state_out && overlap(a.state_in, sbytes, a.state_out, sbytes))
+        return fail(RWKV_ERR_ARG, "state_out overlaps state_in without being equal to it");
+    const size_t abytes_in = (size_t)(B * T * C) * ei, abytes_out = (size_t)(B * T * C) * eo;
+    const void *rd[] = {a.k, a.v, a.r, a.x};
+    for (const void *p : rd)
+        if (overlap(a.y, abytes_out, p, abytes_in)) return fail(RWKV_ERR_ARG, "y overlaps an input");
+    if (a.state_out && (overlap(a.state_out, sbytes, a.y, abytes_out)))
+        return fail(RWKV_ERR_ARG, "state_out overlaps y");
+
+    a.in_f16 = o.in_dtype == RWKV_F16;
+    a.out_f16 = o.out_dtype == RWKV_F16;
+    bool vec = (C % 4) == 0;
+    for (const void *p : ins)
+        if (p && !aligned(p, 4 * ei)) vec = false;
+    if (a.y && !aligned(a.y, 4 * eo)) vec = false;
+    a.vec = vec ? 1 : 0;
+
+    hipError_t e;
+    if (T == 0) {
+        e = launch_passthrough(a, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch (T = 0 state copy)");
+        return ok();
+    }
+    const bool seq = o.algo == RWKV_ALGO_SEQUENTIAL || (o.algo == RWKV_ALGO_AUTO && auto_sequential(B, T, C));
+    if (seq) {
+        e = launch_sequential(a, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch (sequential)");
+        return ok();
+    }
+    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C);
+    const int cmax = chunk_max_len(a.in_f16, a.mode);
+    if (chunk > cmax) {
+        if (o.chunk_len)
+            return fail(RWKV_ERR_ARG, "chunk_len %d exceeds %d, the largest tile this dtype/mode supports",
+                        chunk, cmax);
+        chunk = cmax;
+    }
+    ChunkWorkspace ws{};
+    if (T > chunk) {  // more than one tile per chain: the look-back needs scratch
+        const size_t need = chunk_workspace_bytes(B, T, C, chunk);
+        void *base = o.workspace;
+        if (base) {
+            if (o.workspace_bytes < need)
+                return fail(RWKV_ERR_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                            o.workspace_bytes, need);
+        } else {
+            rwkv_status s = cached_workspace(need, stream, &base);
+            if (s != RWKV_OK) return s;
+        }
+        chunk_workspace_carve(base, B, T, C, chunk, &ws);
+        ws.epoch = next_epoch();
+    }
+    e = launch_chunked(a, chunk, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "launch (chunked)");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                              const void *k, const void *v, void *y, const float *state_in,
+                              float *state_out, hipStream_t stream, const rwkv4_opts *opts) {
+    Resolved o;
+    rwkv_status s = resolve_opts(opts, &o);
+    if (s != RWKV_OK) return s;
+    ForwardArgs a{};
+    a.B = B;
+    a.T = T;
+    a.C = C;
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.r = o.r;
+    a.y = y;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.mode = o.r ? MODE_GATED : MODE_PLAIN;
+    return run_forward(a, o, stream);
+}
+
+rwkv_status rwkv4_wkv_step(int64_t B, int64_t C, const float *w, const float *u, const void *k,
+                           const void *v, const void *r, void *y, float *state, rwkv_dtype in_dtype,
+                           rwkv_dtype out_dtype, hipStream_t stream) {
+    rwkv_status s;
+    if ((s = check_dtype(in_dtype, "in_dtype")) != RWKV_OK) return s;
+    if ((s = check_dtype(out_dtype, "out_dtype")) != RWKV_OK) return s;
+    if (!state) return fail(RWKV_ERR_ARG, "state is required (read and updated in place)");
+    if (!k || !v || !y) return fail(RWKV_ERR_ARG, "k, v and y are required");
+    Resolved o;
+    o.in_dtype = in_dtype;
+    o.out_dtype = out_dtype;
+    o.r = r;
+    o.algo = RWKV_ALGO_SEQUENTIAL;
+    ForwardArgs a{};
+    a.B = B;
+    a.T = 1;
+    a.C = C;
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.r = r;
+    a.y = y;
+    a.state_in = state;
+    a.state_out = state;
+    a.mode = r ? MODE_GATED : MODE_PLAIN;
+    return run_forward(a, o, stream);
+}
+
+rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,
+                                void *x_last, const float *mix_k, const float *mix_v,
+                                const float *mix_r, const void *k, const void *v, const float *w,
+                                const float *u, void *y, void *xk_out, void *xv_out,
+                                const float *state_in, float *state_out, hipStream_t stream,
+                                const rwkv4_opts *opts) {
+    Resolved o;
+    rwkv_status s = resolve_opts(opts, &o);
+    if (s != RWKV_OK) return s;
+    if (o.r) return fail(RWKV_ERR_ARG, "opts->r must be NULL for rwkv4_timemix_fused (r is the mixed x)");
+    if (T > 0 && !x) return fail(RWKV_ERR_ARG, "x is required when T > 0");
+    if (!mix_r) return fail(RWKV_ERR_ARG, "mix_r is required");
+    if (xk_out && !mix_k) return fail(RWKV_ERR_ARG, "xk_out needs mix_k");
+    if (xv_out && !mix_v) return fail(RWKV_ERR_ARG, "xv_out needs mix_v");
+    const size_t ei = esize(o.in_dtype);
+    const size_t act = (size_t)(B > 0 && T > 0 && C > 0 ? B * T * C : 0) * ei;
+    const size_t row = (size_t)(B > 0 && C > 0 ? B * C : 0) * ei;
+    if (overlap(xk_out, act, x, act) || overlap(xv_out, act, x, act) || overlap(xk_out, act, xv_out, act) ||
+        overlap(x_last, row, x, act) || overlap(xk_out, act, k, act) || overlap(xv_out, act, v, act))
+        return fail(RWKV_ERR_ARG, "an output of rwkv4_timemix_fused overlaps an input or another output");
+    ForwardArgs a{};
+    a.B = B;
+    a.T = T;
+    a.C = C;
+    a.w = w;
+    a.u = u;
+    a.k = k;
+    a.v = v;
+    a.x = x;
+    a.x_prev = x_prev;
+    a.x_last = x_last;
+    a.mix_r = mix_r;
+    a.mix_k = mix_k ? mix_k : mix_r;  // unused unless xk_out is set
+    a.mix_v = mix_v ? mix_v : mix_r;  // unused unless xv_out is set
+    a.xk_out = xk_out;
+    a.xv_out = xv_out;
+    a.y = y;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.mode = MODE_TIMEMIX;
+    return run_forward(a, o, stream);
+}
+
+const char *rwkv_status_string(rwkv_status s) {
+    switch (s) {
+        case RWKV_OK: return "ok";
+        case RWKV_ERR_ARG: return "invalid argument";
+        case RWKV_ERR_DTYPE: return "invalid dtype";
+        case RWKV_ERR_ALIGN: return "misaligned pointer";
+        case RWKV_ERR_HIP: return "HIP runtime error";
+        case RWKV_ERR_NOMEM: return "out of device memory";
+    }
+    return "unknown status";
+}
+
+const char *rwkv_last_error(void) { return g_err; }
+
+size_t rwkv4_workspace_bytes(int64_t B, int64_t T, int64_t C, int32_t chunk_len) {
+    if (B < 1 || C < 1 || T < 1) return 0;
+    int chunk = chunk_len > 0 ? chunk_len : auto_chunk_len(B, T, C);
+    if (T <= chunk) return 0;
+    return chunk_workspace_bytes(B, T, C, chunk);
+}
+
+int rwkv_abi_version(void) { return RWKV_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// wkv_internal.h -- internal interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace rwkvwkv {
+
+enum Mode : int {
+    MODE_PLAIN = 0,    // y = wkv
+    MODE_GATED = 1,    // y = sigmoid(r) * wkv, r a [B,T,C] tensor
+    MODE_TIMEMIX = 2,  // token shift prologue, r = xr, y = sigmoid(xr) * wkv
+};
+
+// Everything a forward launch needs; pointers are device memory.
+struct ForwardArgs {
+    int64_t B, T, C;
+    const float *w, *u;
+    const void *k, *v;
+    const void *r;                       // MODE_GATED
+    const void *x, *x_prev;              // MODE_TIMEMIX (x_prev may be null)
+    const float *mix_k, *mix_v, *mix_r;  // MODE_TIMEMIX
+    void *xk_out, *xv_out, *x_last;      // MODE_TIMEMIX, each may be null
+    void *y;
+    const float *state_in;  // may be null (empty state)
+    float *state_out;       // may be null
+    int in_f16, out_f16;
+    int mode;
+    int vec;  // 1: C % 4 == 0 and activation pointers vector-aligned
+};
+
+// Chunked-scan scratch: per tile a flag word and two [3][64] fp32 blocks.
+struct ChunkWorkspace {
+    uint32_t *flags;  // [tiles]
+    float *agg;       // [tiles][3][64] tile aggregate (scan of the tile from the empty state)
+    float *incl;      // [tiles][3][64] state at the end of the tile (inclusive prefix)
+    uint32_t *err;    // one word: set when a look-back wait gave up
+    uint32_t epoch;   // per-launch stamp; flags of other launches never match
+};
+
+constexpr int kTileChannels = 64;  // channels per workgroup tile
+constexpr int kSubLen = 16;        // tokens per lane in the chunked scan
+constexpr int kMinChunk = 64, kMaxChunk = 1024;
+
+// Largest chunk length the chunked kernel supports for a dtype/mode (its register budget).
+int chunk_max_len(int in_f16, int mode);
+// Chunk length (tokens per workgroup tile) the auto policy picks for a shape.
+int auto_chunk_len(int64_t B, int64_t T, int64_t C);
+// True when the auto policy picks the sequential kernel.
+bool auto_sequential(int64_t B, int64_t T, int64_t C);
+// Workspace layout for a chunked launch.
+size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len);
+void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
+                           ChunkWorkspace *ws);
+
+hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
+                          hipStream_t s);
+// T == 0: state_out <- state_in (or the empty state), x_last <- x_prev (or zeros).
+hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s);
+
+}  // namespace rwkvwkv

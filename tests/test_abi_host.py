@@ -1,0 +1,161 @@
+"""Host-only checks of librwkvwkv (no GPU): the library loads, exports every function
+include/rwkvwkv.h declares, and rejects invalid arguments with the documented status
+before anything is enqueued.  The pointers below are fake device addresses: every
+call here fails validation, which runs before any HIP call, so none is dereferenced."""
+import ctypes
+import subprocess
+
+import pytest
+
+import rwkv_wkv_linear_amd as rw
+
+L = rw.lib
+P = 0x7F0000000000  # fake, 256-byte aligned device address
+
+
+def p(off=0):
+    return ctypes.c_void_p(P + off)
+
+
+def opts(**kw):
+    o = rw.Opts()
+    o.size = ctypes.sizeof(rw.Opts)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def fwd(B=2, T=8, C=16, w=p(0x10000), u=p(0x20000), k=p(0x100000), v=p(0x200000), y=p(0x300000),
+        si=None, so=None, o=None):
+    return L.rwkv4_wkv_forward(B, T, C, w, u, k, v, y, si, so, None,
+                               ctypes.byref(o) if o is not None else None)
+
+
+def test_exports_every_declared_function():
+    names = rw.header_functions()
+    assert set(names) >= {"rwkv4_wkv_forward", "rwkv4_wkv_step", "rwkv4_timemix_fused",
+                          "rwkv_status_string", "rwkv_last_error", "rwkv4_workspace_bytes",
+                          "rwkv_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", rw.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in syms, f"{n} not exported by {rw.LIB_PATH}"
+
+
+def test_version_and_strings():
+    assert rw.rwkv_abi_version() == 1
+    for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "invalid dtype"),
+                       (-3, "misaligned pointer"), (-4, "HIP runtime error"),
+                       (-5, "out of device memory")]:
+        assert rw.status_string(code) == text
+    assert rw.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(C=0), dict(T=-1), dict(B=-3)])
+def test_bad_sizes(kw):
+    assert fwd(**kw) == rw.RWKV_ERR_ARG
+    assert "sizes" in rw.rwkv_last_error()
+
+
+@pytest.mark.parametrize("name", ["w", "u", "k", "v", "y"])
+def test_null_required_pointer(name):
+    assert fwd(**{name: None}) == rw.RWKV_ERR_ARG
+
+
+def test_null_kvy_allowed_when_T_is_zero_but_sizes_still_checked():
+    # T = 0 with valid sizes would enqueue a state copy, so only the failing variant runs here
+    assert fwd(T=0, B=0, k=None, v=None, y=None) == rw.RWKV_ERR_ARG
+
+
+def test_too_large():
+    assert fwd(B=1 << 20, T=1 << 20, C=1 << 20) == rw.RWKV_ERR_ARG
+
+
+def test_bad_opts():
+    o = opts(); o.size = 8
+    assert fwd(o=o) == rw.RWKV_ERR_ARG and "opts->size" in rw.rwkv_last_error()
+    assert fwd(o=opts(in_dtype=7)) == rw.RWKV_ERR_DTYPE
+    assert fwd(o=opts(out_dtype=-1)) == rw.RWKV_ERR_DTYPE
+    assert fwd(o=opts(algo=5)) == rw.RWKV_ERR_ARG
+    for c in (32, 100, 2048, -64):
+        assert fwd(o=opts(chunk_len=c)) == rw.RWKV_ERR_ARG, c
+    assert fwd(o=opts(workspace=P + 4, workspace_bytes=1 << 20)) == rw.RWKV_ERR_ALIGN
+
+
+def test_chunk_len_beyond_mode_limit():
+    # gated fp16 keeps three tensors in registers: 512 tokens per tile at most
+    o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, r=P + 0x400000, chunk_len=1024,
+             algo=rw.RWKV_ALGO_CHUNKED)
+    assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "chunk_len" in rw.rwkv_last_error()
+
+
+def test_workspace_too_small():
+    o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, chunk_len=64, algo=rw.RWKV_ALGO_CHUNKED,
+             workspace=P + 0x800000, workspace_bytes=16)
+    assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "workspace" in rw.rwkv_last_error()
+
+
+def test_misaligned():
+    f16 = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16)
+    assert fwd(k=p(0x100001), o=f16) == rw.RWKV_ERR_ALIGN
+    assert fwd(v=p(0x200002)) == rw.RWKV_ERR_ALIGN           # fp32 needs 4-byte alignment
+    assert fwd(y=p(0x300002)) == rw.RWKV_ERR_ALIGN
+    assert fwd(w=p(0x10002)) == rw.RWKV_ERR_ALIGN
+    assert fwd(si=p(0x500002)) == rw.RWKV_ERR_ALIGN
+
+
+def test_aliasing():
+    # state_out partly overlapping state_in
+    assert fwd(si=p(0x500000), so=p(0x500010)) == rw.RWKV_ERR_ARG
+    # y on top of k
+    assert fwd(y=p(0x100000)) == rw.RWKV_ERR_ARG
+    # state_out inside y
+    assert fwd(so=p(0x300000)) == rw.RWKV_ERR_ARG
+
+
+def test_step_validation():
+    s = L.rwkv4_wkv_step
+    args = [4, 16, p(0x10000), p(0x20000), p(0x100000), p(0x200000), None, p(0x300000)]
+    assert s(*args, None, 1, 1, None) == rw.RWKV_ERR_ARG                    # state required
+    assert s(*args, p(0x500000), 3, 1, None) == rw.RWKV_ERR_DTYPE
+    assert s(*args, p(0x500000), 1, 9, None) == rw.RWKV_ERR_DTYPE
+    assert s(0, 16, *args[2:], p(0x500000), 1, 1, None) == rw.RWKV_ERR_ARG   # B = 0
+    a2 = list(args); a2[4] = None
+    assert s(*a2, p(0x500000), 1, 1, None) == rw.RWKV_ERR_ARG                # k required
+
+
+def test_timemix_validation():
+    t = L.rwkv4_timemix_fused
+    B, T, C = 1, 8, 16
+
+    def call(x=p(0x100000), mix_k=p(0x30000), mix_v=p(0x40000), mix_r=p(0x50000), xk=None,
+             o=None):
+        return t(B, T, C, x, None, None, mix_k, mix_v, mix_r, p(0x200000), p(0x300000),
+                 p(0x10000), p(0x20000), p(0x400000), xk, None, None, None, None,
+                 ctypes.byref(o) if o is not None else None)
+
+    assert call(o=opts(r=P + 0x900000)) == rw.RWKV_ERR_ARG and "opts->r" in rw.rwkv_last_error()
+    assert call(mix_r=None) == rw.RWKV_ERR_ARG
+    assert call(x=None) == rw.RWKV_ERR_ARG
+    assert call(mix_k=None, xk=p(0x600000)) == rw.RWKV_ERR_ARG
+    assert call(xk=p(0x100000)) == rw.RWKV_ERR_ARG  # xk_out on top of x
+
+
+def test_last_error_is_thread_local_message():
+    assert fwd(B=0) == rw.RWKV_ERR_ARG
+    msg = rw.rwkv_last_error()
+    assert msg and "B >= 1" in msg
+
+
+def test_workspace_bytes():
+    assert rw.rwkv4_workspace_bytes(1, 64, 64, 64) == 0          # one tile per chain: none needed
+    assert rw.rwkv4_workspace_bytes(0, 64, 64, 0) == 0
+    a = rw.rwkv4_workspace_bytes(1, 65536, 2048, 64)
+    b = rw.rwkv4_workspace_bytes(1, 65536, 2048, 1024)
+    assert a > b > 0
+    # tiles * (64 flags + 2 * 3 * 64 floats) * 4 bytes, plus alignment slack
+    tiles = 32 * 1024
+    assert tiles * 7 * 256 <= a <= tiles * 7 * 256 + 1024

@@ -1,0 +1,277 @@
+"""GPU parity of rwkv4_wkv_forward against the fp64 oracle (element by element).
+
+Covers the RWKV-4 169m workloads at full size (B1 T1024 C768 fp32 ungated from the
+empty state; B8 T1024 C768 fp16 gated from a random prior state), both kernels and
+several tile lengths, and the edge cases: ragged T and C, odd C (per-element path),
+misaligned pointers, T = 1, T = 0, tiny B*C, in-place state, full forgetting,
+shift invariance (k + 100), wide key spreads, split-sequence carry, determinism,
+and negative controls that the gate must reject."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+import wkv_inputs as wi
+from gpu_util import (TOL, canary_ok, check_output, check_state, host, note, poisoned, to_dev,
+                      torch)
+
+_cache = {}
+
+
+def oracle_forward(key, case, method="recurrence"):
+    if key not in _cache:
+        _cache[key] = oracle.forward(case, method=method)
+    return _cache[key]
+
+
+def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
+    import rwkv_wkv_linear_amd as rw
+    B, T, C = case["B"], case["T"], case["C"]
+    odt = y_dtype or case["out_dtype"]
+    y, yfull = poisoned((B, T, C), odt)
+    so, sofull = poisoned((3, B, C), "f32") if state_out else (None, None)
+    note(f"forward {label} B={B} T={T} C={C} in={case['in_dtype']} out={odt} "
+         f"gated={case.get('r') is not None} prior={case.get('state_in') is not None} "
+         f"algo={algo} chunk={chunk_len}")
+    rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
+                         y=y, state_in=to_dev(case.get("state_in")), state_out=so,
+                         r=to_dev(case.get("r")), chunk_len=chunk_len, algo=algo)
+    torch().cuda.synchronize()
+    assert canary_ok(yfull, B * T * C), "write past the end of y"
+    if so is not None:
+        assert canary_ok(sofull, 3 * B * C), "write past the end of state_out"
+    return host(y), (host(so) if so is not None else None)
+
+
+ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("chunked", 256), ("chunked", 512),
+         ("auto", 0)]
+
+
+# ----------------------------------------------------------------------------- small, ragged
+
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("f32", "f16")])
+@pytest.mark.parametrize("algo,chunk", ALGOS)
+def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
+    # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64
+    case = wi.forward_case(2, 1000, 200, seed=41, in_dtype=in_dt, out_dtype=out_dt, gated=True, prior=True)
+    ref = oracle_forward(("ragged", in_dt), case)
+    y, st = run(case, algo, chunk, label="ragged")
+    tol = TOL[in_dt] if out_dt == "f32" or in_dt == "f16" else TOL["f16"]
+    check_output(y, ref, tol, f"ragged {in_dt}->{out_dt} {algo}/{chunk}")
+    check_state(st, ref, TOL[in_dt], f"ragged {in_dt} {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 256)])
+def test_odd_channels(C, algo, chunk):
+    # C % 4 != 0 takes the per-element path; C < 64 leaves most of a tile masked
+    case = wi.forward_case(3, 300, C, seed=42, in_dtype="f16", gated=True, prior=True)
+    ref = oracle_forward(("odd", C), case)
+    y, st = run(case, algo, chunk, label=f"odd C={C}")
+    check_output(y, ref, TOL["f16"], f"C={C} {algo}/{chunk}", argmax=C > 1)
+    check_state(st, ref, TOL["f16"], f"C={C} {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64)])
+def test_misaligned_pointers(algo, chunk):
+    """Tensors offset by one element: the library must take the per-element path."""
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, 130, 64, seed=43, in_dtype="f16", gated=True, prior=True)
+    ref = oracle_forward("misaligned", case)
+
+    def shifted(a):
+        buf = t.empty(a.size + 1, dtype=t.float16, device="cuda:0")
+        view = buf[1:].view(*a.shape)
+        view.copy_(to_dev(a))
+        return view
+
+    k, v, r = shifted(case["k"]), shifted(case["v"]), shifted(case["r"])
+    assert k.data_ptr() % 8 != 0
+    ybuf = t.full((2 * 130 * 64 + 1,), float("nan"), dtype=t.float16, device="cuda:0")
+    y = ybuf[1:].view(2, 130, 64)
+    so = t.empty((3, 2, 64), dtype=t.float32, device="cuda:0")
+    note(f"forward misaligned {algo}/{chunk}")
+    rw.rwkv4_wkv_forward(k, v, to_dev(case["w"]), to_dev(case["u"]), y=y, state_in=to_dev(case["state_in"]),
+                         state_out=so, r=r, algo=algo, chunk_len=chunk)
+    t.cuda.synchronize()
+    check_output(host(y), ref, TOL["f16"], f"misaligned {algo}")
+    check_state(host(so), ref, TOL["f16"], f"misaligned {algo}")
+
+
+@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+def test_single_token(algo):
+    case = wi.forward_case(4, 1, 96, seed=44, in_dtype="f32", gated=True, prior=True)
+    ref = oracle.forward(case, method="direct")
+    y, st = run(case, algo, 64 if algo == "chunked" else 0, label="T=1")
+    check_output(y, ref, TOL["f32"], f"T=1 {algo}")
+    check_state(st, ref, TOL["f32"], f"T=1 {algo}")
+
+
+def test_zero_tokens_copies_state():
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, 4, 40, seed=45, in_dtype="f32", prior=True)
+    si = to_dev(case["state_in"])
+    so = t.full((3, 2, 40), float("nan"), device="cuda:0")
+    k = t.empty((2, 0, 40), device="cuda:0")
+    note("forward T=0")
+    rw.rwkv4_wkv_forward(k, k.clone(), to_dev(case["w"]), to_dev(case["u"]), state_in=si, state_out=so)
+    t.cuda.synchronize()
+    assert np.array_equal(host(so), case["state_in"].astype(np.float64))
+    so2 = t.full((3, 2, 40), float("nan"), device="cuda:0")
+    rw.rwkv4_wkv_forward(k, k.clone(), to_dev(case["w"]), to_dev(case["u"]), state_out=so2)
+    t.cuda.synchronize()
+    s2 = host(so2)
+    assert np.all(s2[0] == 0) and np.all(s2[1] == 0) and np.all(s2[2] < -1e37)
+
+
+def test_state_in_place_and_null_state():
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, 700, 128, seed=46, in_dtype="f16", gated=True, prior=True)
+    ref = oracle_forward("inplace", case)
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+        st = to_dev(case["state_in"])
+        y = t.empty((2, 700, 128), dtype=t.float16, device="cuda:0")
+        note(f"forward in-place state {algo}/{chunk}")
+        rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
+                             y=y, state_in=st, state_out=st, r=to_dev(case["r"]), algo=algo, chunk_len=chunk)
+        t.cuda.synchronize()
+        check_output(host(y), ref, TOL["f16"], f"in-place {algo}/{chunk}")
+        check_state(host(st), ref, TOL["f16"], f"in-place {algo}/{chunk}")
+        y2 = t.empty_like(y)
+        rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
+                             y=y2, state_in=to_dev(case["state_in"]), state_out=None,
+                             r=to_dev(case["r"]), algo=algo, chunk_len=chunk)
+        t.cuda.synchronize()
+        assert t.equal(y, y2)
+
+
+def test_full_forgetting_channels():
+    case = wi.forward_case(1, 400, 64, seed=47, in_dtype="f32", prior=True)
+    case["w"] = case["w"].copy()
+    case["w"][::3] = -np.inf
+    ref = oracle.forward(case, method="direct")
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+        y, st = run(case, algo, chunk, label="w=-inf")
+        check_output(y, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
+        check_state(st, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("shift", [100.0, -100.0])
+def test_shift_invariance_needs_max_trick(shift):
+    """k + 100 overflows e^k in fp32 without the max-trick; the output must not change."""
+    base = wi.forward_case(2, 500, 96, seed=48, in_dtype="f32", gated=True, prior=True)
+    case = dict(base)
+    case["k"] = (base["k"].astype(np.float64) + shift).astype(np.float32)
+    st = base["state_in"].copy()
+    st[2] = st[2] + shift
+    case["state_in"] = st
+    ref = oracle.forward(case)
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 512)):
+        y, s = run(case, algo, chunk, label=f"shift {shift}")
+        check_output(y, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
+        check_state(s, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
+
+
+def test_wide_key_spread():
+    """Keys spread over +-60 nats (beyond fp32's exponent range as plain e^k)."""
+    case = wi.forward_case(1, 600, 64, seed=49, in_dtype="f32", prior=True)
+    g = np.random.default_rng(49)
+    case["k"] = g.uniform(-60, 60, case["k"].shape).astype(np.float32)
+    ref = oracle.forward(case)
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+        y, s = run(case, algo, chunk, label="wide spread")
+        check_output(y, ref, TOL["f32"], f"spread {algo}/{chunk}")
+        check_state(s, ref, TOL["f32"], f"spread {algo}/{chunk}")
+
+
+def test_split_sequence_carry():
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, 900, 128, seed=50, in_dtype="f32", gated=True, prior=True)
+    ref = oracle_forward("split", case)
+    T1 = 333
+    dk, dv, dr = to_dev(case["k"]), to_dev(case["v"]), to_dev(case["r"])
+    w, u = to_dev(case["w"]), to_dev(case["u"])
+    st = to_dev(case["state_in"])
+    note("forward split carry")
+    y1 = rw.rwkv4_wkv_forward(dk[:, :T1].contiguous(), dv[:, :T1].contiguous(), w, u, state_in=st,
+                              state_out=st, r=dr[:, :T1].contiguous(), algo="chunked", chunk_len=64)
+    y2 = rw.rwkv4_wkv_forward(dk[:, T1:].contiguous(), dv[:, T1:].contiguous(), w, u, state_in=st,
+                              state_out=st, r=dr[:, T1:].contiguous(), algo="chunked", chunk_len=128)
+    t.cuda.synchronize()
+    y = np.concatenate([host(y1), host(y2)], axis=1)
+    check_output(y, ref, TOL["f32"], "split carry")
+    check_state(host(st), ref, TOL["f32"], "split carry")
+
+
+def test_deterministic():
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, 2048, 256, seed=51, in_dtype="f16", gated=True, prior=True)
+    args = [to_dev(case[n]) for n in ("k", "v", "w", "u")]
+    outs = []
+    for _ in range(2):
+        note("forward determinism")
+        so = t.empty((3, 2, 256), device="cuda:0")
+        y = rw.rwkv4_wkv_forward(*args, state_in=to_dev(case["state_in"]), state_out=so,
+                                 r=to_dev(case["r"]), algo="chunked", chunk_len=64)
+        t.cuda.synchronize()
+        outs.append((y.clone(), so.clone()))
+    assert t.equal(outs[0][0], outs[1][0]) and t.equal(outs[0][1], outs[1][1])
+
+
+def test_negative_controls_fail_the_gate():
+    """Known-wrong references (the port report's kill-WKV control and its relatives) must
+    miss the gate by far: the metric can tell a working recurrence from a broken one."""
+    from oracle import compare as cmp
+    case = wi.forward_case(2, 512, 128, seed=52, in_dtype="f32", gated=True, prior=True)
+    ref = oracle.forward(case)
+    y, _ = run(case, "chunked", 128, label="negative controls")
+    tol = TOL["f32"]
+    assert cmp.scaled_error(y, ref["y"], ref["scale"]) <= tol
+    g = 1.0 / (1.0 + np.exp(-case["r"].astype(np.float64)))
+    wrong = {
+        "kill-WKV (y = v)": case["v"].astype(np.float64) * g,
+        "no decay (w = 0)": oracle.forward(dict(case, w=np.zeros_like(case["w"])))["y"],
+        "no bonus (u = 0)": oracle.forward(dict(case, u=np.zeros_like(case["u"])))["y"],
+        "prior state ignored": oracle.forward(dict(case, state_in=None))["y"],
+        "gate dropped": oracle.forward(dict(case, r=None))["y"],
+    }
+    for name, yw in wrong.items():
+        e = cmp.scaled_error(y, yw, ref["scale"])
+        note(f"negative control {name}: scaled error {e:.3e}")
+        assert e > 100 * tol, f"negative control '{name}' passes the gate (error {e:.3e})"
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("algo,chunk", ALGOS)
+def test_workload_169m_fp32(algo, chunk):
+    """B1 T1024 C768, fp32 k, v ~ N(0,1), empty state, y = wkv (fp32): bar 1e-5."""
+    case = wi.workload_inputs(0)
+    ref = oracle_forward("w0", case, method="direct")
+    y, st = run(case, algo, chunk, label="rwkv4-169m fp32")
+    check_output(y, ref, TOL["f32"], f"169m fp32 {algo}/{chunk}")
+    check_state(st, ref, TOL["f32"], f"169m fp32 {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("algo,chunk", ALGOS)
+def test_workload_169m_batch_f16(algo, chunk):
+    """B8 T1024 C768, fp16 k, v, r, random prior state, y = sigmoid(r) wkv (fp16): bar 2e-3."""
+    case = wi.workload_inputs(1)
+    ref = oracle_forward("w1", case)
+    if "w1pts" not in _cache:
+        g = np.random.default_rng(7)
+        pts = (g.integers(0, 8, 3000), g.integers(0, 1024, 3000), g.integers(0, 768, 3000))
+        yp, sp = oracle.wkv_points(case["k"], case["v"], case["w"], case["u"], pts, r=case["r"],
+                                   state_in=case["state_in"])
+        # the recurrence form the full comparison uses agrees with the direct sums here
+        assert np.max(np.abs(yp - ref["y"][pts]) / sp) < 1e-12
+        _cache["w1pts"] = True
+    y, st = run(case, algo, chunk, label="rwkv4-169m batch f16")
+    check_output(y, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}")
+    check_state(st, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}")
