@@ -46,6 +46,14 @@ class RwkvError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run: python -m rwkv_wkv_linear_amd.build")
+    # torch ships its own HIP runtime (SONAME libamdhip64.so.7, loaded by its unversioned
+    # file name).  Loading torch first makes the library's libamdhip64.so.7 dependency
+    # resolve to that same runtime; loading the library first would leave two HIP runtimes
+    # in the process, and the second one to initialise finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, fp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
     lib.rwkv4_wkv_forward.argtypes = [i64, i64, i64, fp, fp, vp, vp, vp, fp, fp, vp, ctypes.POINTER(Opts)]

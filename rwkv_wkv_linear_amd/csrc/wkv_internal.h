@@ -31,11 +31,11 @@ struct ForwardArgs {
     int vec;  // 1: C % 4 == 0 and activation pointers vector-aligned
 };
 
-// Chunked-scan scratch: per tile a flag word and two [3][64] fp32 blocks.
+// Chunked-scan scratch: per tile 64 flag words and two [4][64] fp32 state blocks.
 struct ChunkWorkspace {
-    uint32_t *flags;  // [tiles]
-    float *agg;       // [tiles][3][64] tile aggregate (scan of the tile from the empty state)
-    float *incl;      // [tiles][3][64] state at the end of the tile (inclusive prefix)
+    uint32_t *flags;  // [tiles][64] one word per channel: (epoch << 2) | kind
+    float *agg;       // [tiles][4][64] tile aggregate (scan of the tile from the empty state)
+    float *incl;      // [tiles][4][64] state at the end of the tile (inclusive prefix)
     uint32_t *err;    // one word: set when a look-back wait gave up
     uint32_t epoch;   // per-launch stamp; flags of other launches never match
 };

@@ -15,10 +15,16 @@
 // One of the two factors in each step is exactly 1, so each costs one
 // exponential: e^{-|d|} with d the difference of the two candidates.
 //
-// Spans compose: the state after a span of n tokens, started from (a1, b1, p1),
-// is (a1, b1, p1 + n w) merged with the span's own summary from the empty state,
-// by the same max rule.  This operator is associative, which the chunked scan
-// uses to split T across lanes and workgroups.
+// The running max is kept as an anchor key and an age, p = key + n w: the largest
+// term is always some token's key decayed n steps (or the prior state's pp).
+// Every difference of candidates is then formed as (key - k_t) + (small terms),
+// which is exact for nearby keys (Sterbenz), so the rounding of p does not grow
+// with |k| or accumulate over steps as p <- p + w would.
+//
+// Spans compose: the state after a span of L tokens, started from s, is s aged by
+// L merged with the span's own summary from the empty state, by the same max rule.
+// This operator is associative, which the chunked scan uses to split T across
+// lanes and workgroups.
 //
 // Kernels:
 //   wkv_seq_kernel    one lane per (b, 4 channels), loops over T (large B*C, decode).
@@ -44,6 +50,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyP = -1.0e38f;  // p of the empty state (finite, so differences stay defined)
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
 constexpr uint32_t kMaxSpins = 1u << 20;  // ~25 ms of polling before a look-back gives up
+constexpr int kMaxAnchorGap = 32;         // largest spacing of anchor tiles in a chain
 
 template <typename T> struct Raw;
 template <> struct Raw<float> { using type = f4; };
@@ -53,41 +60,46 @@ __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x *
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 struct St {
-    float a, b, p;
+    float a, b;  // numerator and denominator scaled by e^{-p}
+    float k;     // anchor key of the largest term
+    float n;     // its age in tokens: p = k + n * w
 };
 
-__device__ __forceinline__ St st_empty() { return St{0.f, 0.f, kEmptyP}; }
+__device__ __forceinline__ St st_empty() { return St{0.f, 0.f, kEmptyP, 0.f}; }
 
-// Decay exponent of n tokens (0 when n == 0, also for w = -inf).
-__device__ __forceinline__ float span_decay(int64_t n, float w) { return n ? (float)n * w : 0.f; }
+// w = -inf (full forgetting) is carried as a large finite decay, so that 0 * w stays 0;
+// e^{-1e30} and e^{-inf} are both exactly 0 in fp32.
+__device__ __forceinline__ float finite_decay(float w) { return fmaxf(w, -1.0e30f); }
 
-// State s, then a span whose own summary (from the empty state) is t; dec = n * w.
-__device__ __forceinline__ St combine(St s, St t, float dec) {
-    const float P = s.p + dec;
-    const float d = P - t.p;
+__device__ __forceinline__ St st_load(float aa, float bb, float pp) { return St{aa, bb, pp, 0.f}; }
+__device__ __forceinline__ float st_logmax(const St &s, float w) { return fmaf(s.n, w, s.k); }
+
+// State s, then L tokens whose own summary (from the empty state) is t.
+__device__ __forceinline__ St combine(const St &s, const St &t, float L, float w) {
+    const float d = (s.k - t.k) + (s.n + L - t.n) * w;  // p_s + L w - p_t
     const float e = ex(-fabsf(d));
     const bool left = d >= 0.f;
     const float e1 = left ? 1.f : e, e2 = left ? e : 1.f;
-    return St{s.a * e1 + t.a * e2, s.b * e1 + t.b * e2, left ? P : t.p};
+    return St{s.a * e1 + t.a * e2, s.b * e1 + t.b * e2, left ? s.k : t.k, left ? s.n + L : t.n};
 }
 
 // Absorb token (k, v).
 __device__ __forceinline__ void absorb(St &s, float w, float k, float v) {
-    const float pw = s.p + w;
-    const float d = pw - k;
+    const float n1 = s.n + 1.f;
+    const float d = fmaf(n1, w, s.k - k);  // p + w - k
     const float e = ex(-fabsf(d));
     const bool left = d >= 0.f;
     const float e1 = left ? 1.f : e, e2 = left ? e : 1.f;
     s.a = s.a * e1 + v * e2;
     s.b = s.b * e1 + e2;
-    s.p = left ? pw : k;
+    s.k = left ? s.k : k;
+    s.n = left ? n1 : 0.f;
 }
 
 // Numerator and denominator of the output at token (k, v) with bonus u.
-__device__ __forceinline__ void emit(const St &s, float u, float k, float v, float &num,
+__device__ __forceinline__ void emit(const St &s, float w, float u, float k, float v, float &num,
                                      float &den) {
-    const float ku = u + k;
-    const float d = s.p - ku;
+    const float d = (s.k - k) + fmaf(s.n, w, -u);  // p - (u + k)
     const float e = ex(-fabsf(d));
     const bool left = d >= 0.f;
     const float e1 = left ? 1.f : e, e2 = left ? e : 1.f;
@@ -157,9 +169,10 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
     St s[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+        w[q] = finite_decay(w[q]);
         s[q] = st_empty();
         if (a.state_in && q < nch)
-            s[q] = St{a.state_in[sc + q], a.state_in[BC + sc + q], a.state_in[2 * BC + sc + q]};
+            s[q] = st_load(a.state_in[sc + q], a.state_in[BC + sc + q], a.state_in[2 * BC + sc + q]);
     }
     float mk[4], mv[4], mr[4], xs[4];
     if constexpr (MODE == MODE_TIMEMIX) {
@@ -186,7 +199,7 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
         for (int q = 0; q < 4; ++q) {
             const float kk = (float)kr[q], vv = (float)vr[q];
             float num, den;
-            emit(s[q], u[q], kk, vv, num, den);
+            emit(s[q], w[q], u[q], kk, vv, num, den);
             float g = 1.f;
             if constexpr (MODE == MODE_GATED) g = 1.f + ex(-(float)gr[q]);
             if constexpr (MODE == MODE_TIMEMIX) {
@@ -212,7 +225,7 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
             if (q < nch) {
                 a.state_out[sc + q] = s[q].a;
                 a.state_out[BC + sc + q] = s[q].b;
-                a.state_out[2 * BC + sc + q] = s[q].p;
+                a.state_out[2 * BC + sc + q] = st_logmax(s[q], w[q]);
             }
     }
     if constexpr (MODE == MODE_TIMEMIX) {
@@ -224,62 +237,67 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
 // Chunked scan.
 
 __device__ __forceinline__ void publish(const ChunkWorkspace &ws, int64_t tile, uint32_t kind,
-                                        St s, int ch) {
-    float *dst = (kind == kIncl ? ws.incl : ws.agg) + tile * (3 * kTileChannels);
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(dst) + ch, __float_as_uint(s.a),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(dst) + kTileChannels + ch, __float_as_uint(s.b),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(dst) + 2 * kTileChannels + ch,
-                       __float_as_uint(s.p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                        const St &s, int ch) {
+    uint32_t *dst = reinterpret_cast<uint32_t *>(kind == kIncl ? ws.incl : ws.agg) + tile * (4 * kTileChannels);
+    const float f[4] = {s.a, s.b, s.k, s.n};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        __hip_atomic_store(dst + m * kTileChannels + ch, __float_as_uint(f[m]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     // release: this lane's data before this lane's flag (one flag word per channel)
     __hip_atomic_store(ws.flags + tile * kTileChannels + ch, (ws.epoch << 2) | kind,
                        __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Incoming state of tile tt of a chain: walk back over earlier tiles, folding their
-// aggregates, until one has published its inclusive state.
-__device__ St lookback(const ChunkWorkspace &ws, int64_t chain, int64_t tt, float wc, int TW,
+// Incoming state of tile tt >= 1 of a chain.  Anchor tiles (every M-th, tile 0 included)
+// publish their inclusive state; the others publish only their own aggregate.  With a the
+// last anchor before tt, the prefix is INCL(a) + AGG(a+1) + ... + AGG(tt-1), folded in that
+// fixed order whatever the timing, so results are bitwise reproducible.  All the flags are
+// polled together: one round trip, not one per tile.
+__device__ St lookback(const ChunkWorkspace &ws, int64_t chain, int64_t tt, float wc, int TW, int M,
                        int ch) {
-    St acc = st_empty();
-    int64_t acc_len = 0;
-    for (int64_t kk = tt - 1; kk >= 0; --kk) {
-        const int64_t tile = chain + kk;
-        uint32_t f = 0, spins = 0;
-        for (;;) {
-            f = __hip_atomic_load(ws.flags + tile * kTileChannels + ch, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            if ((f >> 2) == ws.epoch) {
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                break;
+    const int64_t a = ((tt - 1) / M) * M;
+    const int cnt = (int)(tt - a);  // tiles a .. tt-1, 1 <= cnt <= M <= kMaxAnchorGap
+    uint32_t spins = 0;
+    for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int m = 0; m < kMaxAnchorGap; ++m) {
+            if (m < cnt) {
+                const uint32_t f = __hip_atomic_load(ws.flags + (chain + a + m) * kTileChannels + ch,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                all = all && (f >> 2) == ws.epoch;
             }
-            ++spins;
-            // give up after kMaxSpins, or at once when another wait has already given up
-            if (spins > kMaxSpins ||
-                ((spins & 255u) == 0 &&
-                 __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-                atomicOr(ws.err, 1u);
-                f = 0;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
         }
-        const uint32_t kind = f & 3u;
-        if (kind == 0) {  // gave up: poison the tile so the failure shows in its outputs
-            acc = St{__builtin_nanf(""), __builtin_nanf(""), 0.f};
+        if (all) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             break;
         }
-        const uint32_t *src =
-            reinterpret_cast<const uint32_t *>(kind == kIncl ? ws.incl : ws.agg) + tile * (3 * kTileChannels);
-        St x;
-        x.a = __uint_as_float(__hip_atomic_load(src + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        x.b = __uint_as_float(
-            __hip_atomic_load(src + kTileChannels + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        x.p = __uint_as_float(
-            __hip_atomic_load(src + 2 * kTileChannels + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        acc = combine(x, acc, span_decay(acc_len, wc));
-        acc_len += TW;
-        if (kind == kIncl) break;
+        ++spins;
+        // give up after kMaxSpins, or at once when another wait has already given up
+        if (spins > kMaxSpins ||
+            ((spins & 255u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+            atomicOr(ws.err, 1u);
+            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};  // poison the tile's outputs
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    St acc = st_empty();
+    float acc_len = 0.f;
+#pragma unroll
+    for (int m = kMaxAnchorGap - 1; m >= 0; --m) {
+        if (m < cnt) {
+            const int64_t tile = chain + a + m;
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(m == 0 ? ws.incl : ws.agg) + tile * (4 * kTileChannels);
+            float x[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                x[f] = __uint_as_float(
+                    __hip_atomic_load(src + f * kTileChannels + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            acc = combine(St{x[0], x[1], x[2], x[3]}, acc, acc_len, wc);
+            acc_len += (float)TW;
+        }
     }
     return acc;
 }
@@ -293,13 +311,15 @@ constexpr int chunk_max_threads() {
 // blockIdx = tt * (B * nCT) + b * nCT + ct, so every tile a workgroup waits for has a
 // lower index and was dispatched earlier.  Thread = (sub-chunk j, channel group g):
 // tid = j * 16 + g, channels ct*64 + 4g .. +3, tokens tt*TW + 16j .. +15.
+// LDS: per sub-chunk and channel the four fields of a state, then the tile's incoming state.
 template <typename TIn, typename TOut, int MODE>
 __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
-    wkv_chunk_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW) {
+    wkv_chunk_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
     constexpr int L = kSubLen, G = 16, CW = kTileChannels;
     using R = typename Raw<TIn>::type;
     extern __shared__ float smem[];
-    float *sA = smem, *sB = smem + S * CW, *sP = smem + 2 * S * CW, *sI = smem + 3 * S * CW;
+    float *sF[4] = {smem, smem + S * CW, smem + 2 * S * CW, smem + 3 * S * CW};
+    float *sI = smem + 4 * S * CW;  // [4][CW]
 
     const int tid = threadIdx.x, g = tid % G, j = tid / G;
     const int64_t BCT = a.B * nCT;
@@ -322,6 +342,8 @@ __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
     float w[4], u[4];
     load_param4(a.w, c0, nch, w);
     load_param4(a.u, c0, nch, u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = finite_decay(w[q]);
 
     // Phase A: every load of the lane's tile slice is issued up front.
     const int64_t base = (b * a.T + t0) * a.C + c0;
@@ -361,9 +383,10 @@ __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int idx = j * CW + g * 4 + q;
-        sA[idx] = sum[q].a;
-        sB[idx] = sum[q].b;
-        sP[idx] = sum[q].p;
+        sF[0][idx] = sum[q].a;
+        sF[1][idx] = sum[q].b;
+        sF[2][idx] = sum[q].k;
+        sF[3][idx] = sum[q].n;
     }
     __syncthreads();
 
@@ -373,47 +396,48 @@ __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
         const int ch = tid;
         const int64_t c = ct * CW + ch;
         const bool cok = c < a.C;
-        const float wc = cok ? a.w[c] : 0.f;
+        const float wc = cok ? finite_decay(a.w[c]) : 0.f;
         St run = st_empty();
+        float run_len = 0.f;
         for (int jj = 0; jj < S; ++jj) {
             const int64_t len = std::max<int64_t>(0, std::min<int64_t>(L, a.T - (tile_t0 + (int64_t)jj * L)));
             const int idx = jj * CW + ch;
-            const St cur = St{sA[idx], sB[idx], sP[idx]};
-            sA[idx] = run.a;
-            sB[idx] = run.b;
-            sP[idx] = run.p;
-            run = combine(run, cur, span_decay(len, wc));
+            const St cur = St{sF[0][idx], sF[1][idx], sF[2][idx], sF[3][idx]};
+            sF[0][idx] = run.a;
+            sF[1][idx] = run.b;
+            sF[2][idx] = run.k;
+            sF[3][idx] = run.n;
+            run = combine(run, cur, (float)len, wc);
+            run_len += (float)len;
         }
         St prefix = st_empty();
         if (tt == 0 && a.state_in && cok) {
             const int64_t s = b * a.C + c;
-            prefix = St{a.state_in[s], a.state_in[BC + s], a.state_in[2 * BC + s]};
+            prefix = st_load(a.state_in[s], a.state_in[BC + s], a.state_in[2 * BC + s]);
         }
-        if (nTT > 1 && tt < nTT - 1) {
+        if (nTT > 1) {
             const int64_t chain = (b * nCT + ct) * nTT;
-            if (tt > 0) {
-                publish(ws, chain + tt, kAgg, run, ch);
-                prefix = lookback(ws, chain, tt, wc, TW, ch);
-            }
-            publish(ws, chain + tt, kIncl, combine(prefix, run, span_decay(tile_len, wc)), ch);
-        } else if (nTT > 1) {
-            prefix = lookback(ws, (b * nCT + ct) * nTT, tt, wc, TW, ch);
+            const bool anchor = (tt % M) == 0, last = tt == nTT - 1;
+            if (!anchor && !last) publish(ws, chain + tt, kAgg, run, ch);
+            if (tt > 0) prefix = lookback(ws, chain, tt, wc, TW, M, ch);
+            if (anchor && !last) publish(ws, chain + tt, kIncl, combine(prefix, run, run_len, wc), ch);
         }
         sI[ch] = prefix.a;
         sI[CW + ch] = prefix.b;
-        sI[2 * CW + ch] = prefix.p;
+        sI[2 * CW + ch] = prefix.k;
+        sI[3 * CW + ch] = prefix.n;
     }
     __syncthreads();
 
     // Phase D: the lane's starting state = tile prefix, then the sub-chunks before it.
     St st[4];
-    const int64_t before = std::min<int64_t>((int64_t)j * L, tile_len);
+    const float before = (float)std::min<int64_t>((int64_t)j * L, tile_len);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int cl = g * 4 + q;
-        const St pre = St{sI[cl], sI[CW + cl], sI[2 * CW + cl]};
-        const St exl = St{sA[j * CW + cl], sB[j * CW + cl], sP[j * CW + cl]};
-        st[q] = combine(pre, exl, span_decay(before, w[q]));
+        const int cl = g * 4 + q, jl = j * CW + cl;
+        const St pre = St{sI[cl], sI[CW + cl], sI[2 * CW + cl], sI[3 * CW + cl]};
+        const St exl = St{sF[0][jl], sF[1][jl], sF[2][jl], sF[3][jl]};
+        st[q] = combine(pre, exl, before, w[q]);
     }
 
     // Phase E: replay the tokens from registers, emit y.
@@ -429,7 +453,7 @@ __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
             for (int q = 0; q < 4; ++q) {
                 const float kk = (float)kr[i][q], vv = (float)vr[i][q];
                 float num, den;
-                emit(st[q], u[q], kk, vv, num, den);
+                emit(st[q], w[q], u[q], kk, vv, num, den);
                 float gt = 1.f;
                 if constexpr (MODE == MODE_GATED) gt = 1.f + ex(-(float)gr[i][q]);
                 if constexpr (MODE == MODE_TIMEMIX) {
@@ -460,7 +484,7 @@ __global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
                 if (q < nch) {
                     a.state_out[sc + q] = st[q].a;
                     a.state_out[BC + sc + q] = st[q].b;
-                    a.state_out[2 * BC + sc + q] = st[q].p;
+                    a.state_out[2 * BC + sc + q] = st_logmax(st[q], w[q]);
                 }
         }
         if constexpr (MODE == MODE_TIMEMIX) {
@@ -510,10 +534,13 @@ hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorksp
     const int nCT = (int)((a.C + kTileChannels - 1) / kTileChannels);
     const int nTT = (int)((a.T + chunk_len - 1) / chunk_len);
     const int64_t blocks = a.B * (int64_t)nCT * nTT;
-    const size_t lds = (size_t)(3 * S * kTileChannels + 3 * kTileChannels) * sizeof(float);
+    const size_t lds = (size_t)(4 * S * kTileChannels + 4 * kTileChannels) * sizeof(float);
     if (blocks > 0x7fffffff || 16 * S > chunk_max_threads<TIn, MODE>()) return hipErrorInvalidConfiguration;
+    // anchor spacing ~ sqrt(tiles per chain): the anchor chain and each tile's fold stay short
+    int M = 4;
+    while (M < kMaxAnchorGap && (int64_t)M * M < nTT) M <<= 1;
     hipLaunchKernelGGL((wkv_chunk_kernel<TIn, TOut, MODE>), dim3((unsigned)blocks), dim3(16 * S), lds,
-                       s, a, ws, S, nCT, nTT, chunk_len);
+                       s, a, ws, S, nCT, nTT, chunk_len, M);
     return hipGetLastError();
 }
 
@@ -562,9 +589,9 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
     const int64_t nCT = (C + kTileChannels - 1) / kTileChannels;
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
-    // flags [tiles][64] u32 + agg, incl [tiles][3][64] f32 + one error word, 256-B aligned parts
+    // flags [tiles][64] u32 + agg, incl [tiles][4][64] f32 + one error word, 256-B aligned parts
     auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-    return (size_t)(al(tiles * kTileChannels * 4) + 2 * al(tiles * 3 * kTileChannels * 4) + 256);
+    return (size_t)(al(tiles * kTileChannels * 4) + 2 * al(tiles * 4 * kTileChannels * 4) + 256);
 }
 
 void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
@@ -577,9 +604,9 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
     ws->flags = reinterpret_cast<uint32_t *>(p);
     p += al(tiles * kTileChannels * 4);
     ws->agg = reinterpret_cast<float *>(p);
-    p += al(tiles * 3 * kTileChannels * 4);
+    p += al(tiles * 4 * kTileChannels * 4);
     ws->incl = reinterpret_cast<float *>(p);
-    p += al(tiles * 3 * kTileChannels * 4);
+    p += al(tiles * 4 * kTileChannels * 4);
     ws->err = reinterpret_cast<uint32_t *>(p);
 }
 

@@ -8,7 +8,11 @@ import numpy as np
 
 from oracle import compare as cmp
 
-TOL = {"f32": 1e-5, "f16": 2e-3}   # scaled error bar per input dtype
+TOL = {"f32": 1e-5, "f16": 2e-3}   # scaled error bar of the outputs, per input dtype
+# The fp32 state has no numerator/denominator cancellation: rounding accumulates over the
+# decay window, 1 / (1 - e^w) ~ 149 tokens for the slowest channel (w = -e^-5), at about
+# 4 roundings of 2^-24 per token -> 3.6e-5.  The state bar is this bound, rounded up.
+STATE_TOL_FLOOR = 5e-5
 CANARY = 4096                       # elements after each output that must stay untouched
 
 
@@ -46,24 +50,25 @@ def poisoned(shape, dtype_name):
     n = int(np.prod(shape))
     full = t.full((n + CANARY,), float("nan"), dtype=tdtype(dtype_name) if isinstance(dtype_name, str)
                   else dtype_name, device=dev())
-    full[n:] = 12345.0
+    full[n:] = 1234.0  # exact in fp16 and fp32
     return full[:n].view(*shape), full
 
 
 def canary_ok(full, n):
     tail = full[n:].float().cpu().numpy()
-    return bool(np.all(tail == 12345.0))
+    return bool(np.all(tail == 1234.0))
 
 
 def host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def check_output(y, ref, tol, what, argmax=True):
-    """Gate: scaled error <= tol, no NaN, argmax identical (tie band rule)."""
+def check_output(y, ref, tol, what, argmax=True, out_dtype="f32"):
+    """Gate: scaled error <= tol, no NaN, argmax identical (tie band rule).  With an fp16
+    output the yardstick is floored at fp16's smallest normal (see oracle.compare)."""
     y = np.asarray(y, dtype=np.float64)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output (unwritten element or NaN)"
-    rep = cmp.report(y, ref, tol)
+    rep = cmp.report(y, ref, tol, cmp.FLOOR[out_dtype])
     note(f"{what}: scaled {rep['scaled']:.3e} literal {rep['literal']:.3e} min_cos "
          f"{rep['min_cos']:.12f} argmax_mismatch {rep['argmax_mismatch']}/{rep['argmax_rows']} "
          f"near_ties {rep['near_ties']}")
@@ -74,6 +79,7 @@ def check_output(y, ref, tol, what, argmax=True):
 
 
 def check_state(state, ref, tol, what):
+    tol = max(tol, STATE_TOL_FLOOR)
     ea, eb = cmp.state_error(state, ref["state"], ref["state_abs"])
     note(f"{what}: state err aa {ea:.3e} bb {eb:.3e}")
     assert ea <= tol and eb <= tol, f"{what}: state error aa {ea:.3e} bb {eb:.3e} > {tol:.1e}"

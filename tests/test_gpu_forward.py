@@ -58,7 +58,7 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     ref = oracle_forward(("ragged", in_dt), case)
     y, st = run(case, algo, chunk, label="ragged")
     tol = TOL[in_dt] if out_dt == "f32" or in_dt == "f16" else TOL["f16"]
-    check_output(y, ref, tol, f"ragged {in_dt}->{out_dt} {algo}/{chunk}")
+    check_output(y, ref, tol, f"ragged {in_dt}->{out_dt} {algo}/{chunk}", out_dtype=out_dt)
     check_state(st, ref, TOL[in_dt], f"ragged {in_dt} {algo}/{chunk}")
 
 
@@ -69,7 +69,7 @@ def test_odd_channels(C, algo, chunk):
     case = wi.forward_case(3, 300, C, seed=42, in_dtype="f16", gated=True, prior=True)
     ref = oracle_forward(("odd", C), case)
     y, st = run(case, algo, chunk, label=f"odd C={C}")
-    check_output(y, ref, TOL["f16"], f"C={C} {algo}/{chunk}", argmax=C > 1)
+    check_output(y, ref, TOL["f16"], f"C={C} {algo}/{chunk}", argmax=C > 1, out_dtype="f16")
     check_state(st, ref, TOL["f16"], f"C={C} {algo}/{chunk}")
 
 
@@ -96,7 +96,7 @@ def test_misaligned_pointers(algo, chunk):
     rw.rwkv4_wkv_forward(k, v, to_dev(case["w"]), to_dev(case["u"]), y=y, state_in=to_dev(case["state_in"]),
                          state_out=so, r=r, algo=algo, chunk_len=chunk)
     t.cuda.synchronize()
-    check_output(host(y), ref, TOL["f16"], f"misaligned {algo}")
+    check_output(host(y), ref, TOL["f16"], f"misaligned {algo}", out_dtype="f16")
     check_state(host(so), ref, TOL["f16"], f"misaligned {algo}")
 
 
@@ -139,7 +139,7 @@ def test_state_in_place_and_null_state():
         rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
                              y=y, state_in=st, state_out=st, r=to_dev(case["r"]), algo=algo, chunk_len=chunk)
         t.cuda.synchronize()
-        check_output(host(y), ref, TOL["f16"], f"in-place {algo}/{chunk}")
+        check_output(host(y), ref, TOL["f16"], f"in-place {algo}/{chunk}", out_dtype="f16")
         check_state(host(st), ref, TOL["f16"], f"in-place {algo}/{chunk}")
         y2 = t.empty_like(y)
         rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
@@ -273,5 +273,5 @@ def test_workload_169m_batch_f16(algo, chunk):
         assert np.max(np.abs(yp - ref["y"][pts]) / sp) < 1e-12
         _cache["w1pts"] = True
     y, st = run(case, algo, chunk, label="rwkv4-169m batch f16")
-    check_output(y, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}")
+    check_output(y, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}", out_dtype="f16")
     check_state(st, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}")

@@ -24,13 +24,15 @@ def test_decode_40_layers():
                           to_dev(layer["u"]), st, y=y)
         t.cuda.synchronize()
         assert canary_ok(yfull, 256 * 5120)
-        check_output(host(y), ref, TOL["f16"], f"decode layer {l}", argmax=(l % 8 == 0))
+        check_output(host(y), ref, TOL["f16"], f"decode layer {l}", argmax=(l % 8 == 0), out_dtype="f16")
         check_state(host(st), ref, TOL["f16"], f"decode layer {l}")
 
 
 @pytest.mark.parametrize("gated", [False, True])
 def test_steps_equal_sequential_forward(gated):
-    """T calls of step reproduce the sequential forward over the same T tokens exactly."""
+    """T calls of step reproduce a forward over the same T tokens.  Not bitwise: the
+    forward carries the running max as (anchor key, age) across tokens, while each step
+    call rounds it to pp = key + age * w once when it stores the state."""
     import rwkv_wkv_linear_amd as rw
     t = torch()
     case = wi.forward_case(3, 50, 72, seed=71, in_dtype="f16", gated=gated, prior=True)
@@ -46,11 +48,15 @@ def test_steps_equal_sequential_forward(gated):
         ys.append(rw.rwkv4_wkv_step(k[:, i].contiguous(), v[:, i].contiguous(),
                                     r[:, i].contiguous() if gated else None, w, u, st))
     t.cuda.synchronize()
-    assert t.equal(t.stack(ys, dim=1), yf)
-    assert t.equal(st, so)
     ref = oracle.forward(case)
-    check_output(host(yf), ref, TOL["f16"], f"step chain gated={gated}")
+    check_output(host(yf), ref, TOL["f16"], f"forward gated={gated}", out_dtype="f16")
+    check_output(host(t.stack(ys, dim=1)), ref, TOL["f16"], f"step chain gated={gated}", out_dtype="f16")
+    check_state(host(so), ref, TOL["f16"], f"forward gated={gated}")
     check_state(host(st), ref, TOL["f16"], f"step chain gated={gated}")
+    # the two fp32 paths agree far inside the fp16 output bar
+    d = np.max(np.abs(host(t.stack(ys, dim=1)) - host(yf)) / np.maximum(ref["scale"], 2.0 ** -14))
+    note(f"step chain vs forward: {d:.3e}")
+    assert d <= 1e-3
 
 
 def test_step_fp32_ungated_odd_channels():

@@ -43,7 +43,7 @@ def run(case, algo="auto", chunk_len=0, with_xkv=False, with_prev=True, label=""
 
 def check_all(out, ref, case, what, with_xkv):
     tol = TOL[case["in_dtype"]]
-    check_output(out["y"], ref, tol, what)
+    check_output(out["y"], ref, tol, what, out_dtype=case["out_dtype"])
     check_state(out["state"], ref, tol, what)
     assert np.array_equal(out["x_last"], ref["x_last"]), f"{what}: x_last differs"
     if with_xkv:
