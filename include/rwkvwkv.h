@@ -87,7 +87,8 @@ typedef struct rwkv4_opts {
     const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
     int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto,
-                                else a power of two in [64, 1024] */
+                                else 64 or 128 (fp16) / 64 (fp32): the tile's rows
+                                are staged in the workgroup's LDS */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
                                 else device memory of workspace_bytes >= the size

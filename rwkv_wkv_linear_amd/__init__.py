@@ -4,8 +4,9 @@ Thin ctypes marshalling over the C ABI in include/rwkvwkv.h -- every step of the
 computation runs in the library's HIP kernels.  Functions carry the C names and
 take torch tensors (device memory and streams only); they check shapes, dtypes,
 devices and contiguity, pass data pointers and the current HIP stream, and raise
-RwkvError on a non-OK status.  Importing this package fails if the library is
-not built (``python -m rwkv_wkv_linear_amd.build``); there is no fallback path.
+RwkvError on a non-OK status.  The library loads on first use and raises
+ImportError if it is not built (``python -m rwkv_wkv_linear_amd.build``); there is
+no fallback path.
 """
 from __future__ import annotations
 
@@ -74,7 +75,23 @@ def _load():
     return lib
 
 
-lib = _load()
+_lib = None
+
+
+def _get_lib():
+    """The loaded library (loaded on first use; raises ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):
+    # `rwkv_wkv_linear_amd.lib` loads the library on first access; importing the package
+    # alone does not, so the build step can import it while no library exists yet
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(name)
 
 
 def header_functions(path: str = HEADER_PATH):
@@ -86,7 +103,7 @@ def header_functions(path: str = HEADER_PATH):
 
 
 def status_string(status: int) -> str:
-    return lib.rwkv_status_string(int(status)).decode()
+    return _get_lib().rwkv_status_string(int(status)).decode()
 
 
 def rwkv_status_string(status: int) -> str:
@@ -94,15 +111,15 @@ def rwkv_status_string(status: int) -> str:
 
 
 def rwkv_last_error() -> str:
-    return lib.rwkv_last_error().decode()
+    return _get_lib().rwkv_last_error().decode()
 
 
 def rwkv_abi_version() -> int:
-    return lib.rwkv_abi_version()
+    return _get_lib().rwkv_abi_version()
 
 
 def rwkv4_workspace_bytes(B: int, T: int, C: int, chunk_len: int = 0) -> int:
-    return int(lib.rwkv4_workspace_bytes(B, T, C, chunk_len))
+    return int(_get_lib().rwkv4_workspace_bytes(B, T, C, chunk_len))
 
 
 # ----------------------------------------------------------------------------- tensor marshalling
@@ -189,7 +206,7 @@ def rwkv4_wkv_forward(k, v, w, u, y=None, state_in=None, state_out=None, *, r=No
     _need(workspace, "workspace", device=dev)
     o = _opts(_dtype_code(k.dtype), _dtype_code(odt), r, chunk_len, algo, workspace)
     with torch.cuda.device(dev):
-        _check(lib.rwkv4_wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+        _check(_get_lib().rwkv4_wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                      _ptr(state_in), _ptr(state_out), _stream(stream, dev),
                                      ctypes.byref(o)))
     return y
@@ -211,7 +228,7 @@ def rwkv4_wkv_step(k, v, r, w, u, state, y=None, *, out_dtype=None, stream=None)
         y = torch.empty((B, C), dtype=odt, device=dev)
     _need(y, "y", (B, C), odt, dev)
     with torch.cuda.device(dev):
-        _check(lib.rwkv4_wkv_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(y),
+        _check(_get_lib().rwkv4_wkv_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(y),
                                   _ptr(state), _dtype_code(k.dtype), _dtype_code(odt),
                                   _stream(stream, dev)))
     return y
@@ -244,7 +261,7 @@ def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, x
     _need(workspace, "workspace", device=dev)
     o = _opts(_dtype_code(dt), _dtype_code(odt), None, chunk_len, algo, workspace)
     with torch.cuda.device(dev):
-        _check(lib.rwkv4_timemix_fused(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(mix_k),
+        _check(_get_lib().rwkv4_timemix_fused(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(mix_k),
                                        _ptr(mix_v), _ptr(mix_r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                        _ptr(y), _ptr(xk_out), _ptr(xv_out), _ptr(state_in),
                                        _ptr(state_out), _stream(stream, dev), ctypes.byref(o)))

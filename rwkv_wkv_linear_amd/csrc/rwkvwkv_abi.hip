@@ -167,6 +167,11 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         if (p && !aligned(p, 4 * ei)) vec = false;
     if (a.y && !aligned(a.y, 4 * eo)) vec = false;
     a.vec = vec ? 1 : 0;
+    bool vec16 = (C % (int64_t)(16 / ei)) == 0;
+    for (const void *p : {a.k, a.v, a.r, a.x})
+        if (p && !aligned(p, 16)) vec16 = false;
+    a.vec16 = vec16 ? 1 : 0;
+    a.vec16y = (a.y && aligned(a.y, 16) && (C % (int64_t)(16 / eo)) == 0) ? 1 : 0;
 
     hipError_t e;
     if (T == 0) {

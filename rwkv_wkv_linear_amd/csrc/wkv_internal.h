@@ -28,20 +28,20 @@ struct ForwardArgs {
     float *state_out;       // may be null
     int in_f16, out_f16;
     int mode;
-    int vec;  // 1: C % 4 == 0 and activation pointers vector-aligned
+    int vec;    // 1: C % 4 == 0 and activation pointers aligned for 4-element vectors
+    int vec16;   // 1: input rows split into 16-byte chunks (C % (16 / size) == 0, 16-B aligned)
+    int vec16y;  // 1: the same for y
 };
 
-// Chunked-scan scratch: per tile 64 flag words and two [4][64] fp32 state blocks.
+// Chunked-scan scratch: per tile and channel four 64-bit words (a, b, key, age), each the
+// fp32 value tagged with (epoch << 2 | kind) in its high half.
 struct ChunkWorkspace {
-    uint32_t *flags;  // [tiles][64] one word per channel: (epoch << 2) | kind
-    float *agg;       // [tiles][4][64] tile aggregate (scan of the tile from the empty state)
-    float *incl;      // [tiles][4][64] state at the end of the tile (inclusive prefix)
+    uint64_t *words;  // [tiles][4][64]
     uint32_t *err;    // one word: set when a look-back wait gave up
-    uint32_t epoch;   // per-launch stamp; flags of other launches never match
+    uint32_t epoch;   // per-launch stamp; words of other launches never match
 };
 
 constexpr int kTileChannels = 64;  // channels per workgroup tile
-constexpr int kSubLen = 16;        // tokens per lane in the chunked scan
 constexpr int kMinChunk = 64, kMaxChunk = 1024;
 
 // Largest chunk length the chunked kernel supports for a dtype/mode (its register budget).

@@ -28,11 +28,11 @@
 //
 // Kernels:
 //   wkv_seq_kernel    one lane per (b, 4 channels), loops over T (large B*C, decode).
-//   wkv_chunk_kernel  one workgroup per (b, 64 channels, tile of TW tokens); each lane
-//                     keeps 16 tokens x 4 channels of k, v (and r or x) in VGPRs,
-//                     reduces them to a summary, the workgroup scans the summaries in
-//                     LDS, a decoupled look-back over earlier tiles supplies the
-//                     incoming state, and each lane replays its tokens to emit y.
+//   wkv_tile_kernel   one workgroup per (b, 64 channels, tile of TW tokens); each wave holds
+//                     L tokens of the 64 channels, one lane per channel, in VGPRs from load
+//                     to store.  A lane reduces its tokens to a summary, the waves fold the
+//                     summaries in LDS, a decoupled look-back over earlier tiles supplies the
+//                     tile's incoming state, and each lane replays its tokens to emit y.
 //                     HBM traffic is one read of each input and one write of y.
 //   wkv_passthrough   T = 0: copy the state (and x_prev to x_last).
 
@@ -49,8 +49,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyP = -1.0e38f;  // p of the empty state (finite, so differences stay defined)
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
-constexpr uint32_t kMaxSpins = 1u << 20;  // ~25 ms of polling before a look-back gives up
-constexpr int kMaxAnchorGap = 32;         // largest spacing of anchor tiles in a chain
+constexpr uint32_t kMaxSpins = 1u << 18;  // ~30 ms of polling before a look-back gives up
+constexpr int kMaxAnchorGap = 16;         // spacing of anchor tiles in a chain (S >= 4 waves poll <= 4 each)
 
 template <typename T> struct Raw;
 template <> struct Raw<float> { using type = f4; };
@@ -139,6 +139,19 @@ __device__ __forceinline__ void store4(T *p, int64_t off, int nch, bool vec, con
             if (q < nch) p[off + q] = (T)x[q];
     }
 }
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane l's
+// bytes land at lds + 16 l.  `lds` must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// L values of one channel, one per token, as loaded.
+template <typename T, int L> struct Rows {
+    T p[L];
+    __device__ __forceinline__ float get(int i) const { return (float)p[i]; }
+};
 
 __device__ __forceinline__ void load_param4(const float *p, int64_t c0, int nch, float (&x)[4]) {
 #pragma unroll
@@ -236,259 +249,454 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
 // ------------------------------------------------------------------------------------------
 // Chunked scan.
 
+// Cross-workgroup exchange.  Each published state field is one 64-bit word: the fp32
+// value in the low half, the tag (epoch << 2 | kind) in the high half, written and read
+// as relaxed agent-scope 64-bit atomics.  A reader accepts a tile's state when all four of
+// its words carry the expected tag, so no fence (and no L2 write-back or invalidate) is
+// needed: each word is self-validating and the fields need no mutual order.
 __device__ __forceinline__ void publish(const ChunkWorkspace &ws, int64_t tile, uint32_t kind,
                                         const St &s, int ch) {
-    uint32_t *dst = reinterpret_cast<uint32_t *>(kind == kIncl ? ws.incl : ws.agg) + tile * (4 * kTileChannels);
+    uint64_t *dst = ws.words + tile * (4 * kTileChannels);
+    const uint64_t tag = (uint64_t)((ws.epoch << 2) | kind) << 32;
     const float f[4] = {s.a, s.b, s.k, s.n};
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-        __hip_atomic_store(dst + m * kTileChannels + ch, __float_as_uint(f[m]), __ATOMIC_RELAXED,
+        __hip_atomic_store(dst + m * kTileChannels + ch, tag | __float_as_uint(f[m]), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    // release: this lane's data before this lane's flag (one flag word per channel)
-    __hip_atomic_store(ws.flags + tile * kTileChannels + ch, (ws.epoch << 2) | kind,
-                       __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Incoming state of tile tt >= 1 of a chain.  Anchor tiles (every M-th, tile 0 included)
-// publish their inclusive state; the others publish only their own aggregate.  With a the
-// last anchor before tt, the prefix is INCL(a) + AGG(a+1) + ... + AGG(tt-1), folded in that
-// fixed order whatever the timing, so results are bitwise reproducible.  All the flags are
-// polled together: one round trip, not one per tile.
-__device__ St lookback(const ChunkWorkspace &ws, int64_t chain, int64_t tt, float wc, int TW, int M,
-                       int ch) {
-    const int64_t a = ((tt - 1) / M) * M;
-    const int cnt = (int)(tt - a);  // tiles a .. tt-1, 1 <= cnt <= M <= kMaxAnchorGap
+// Fold of the published states of tiles [lo, hi) of a chain, left to right; tile lo is an
+// anchor (inclusive state) when lo_incl is set, every other tile an aggregate.  Waiting
+// costs one word per tile: lane m polls the last field of channel 0 of tile lo + m, with a
+// back-off, until the wave sees them all tagged; then every lane loads its channel's fields
+// and checks every tag (a word written by the same store instruction for another channel may
+// become visible a little later; that case polls again).  Returns NaNs if the wait gives up
+// (then the failure shows in the outputs and ws.err is set).
+template <int MAXT>
+__device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo, int64_t hi, bool lo_incl,
+                             float wc, float TW, int ch) {
+    const int cnt = (int)(hi - lo);
+    const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
+    uint64_t w[MAXT][4];
     uint32_t spins = 0;
     for (;;) {
-        bool all = true;
-#pragma unroll
-        for (int m = 0; m < kMaxAnchorGap; ++m) {
-            if (m < cnt) {
-                const uint32_t f = __hip_atomic_load(ws.flags + (chain + a + m) * kTileChannels + ch,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                all = all && (f >> 2) == ws.epoch;
-            }
+        // cheap readiness probe: one word per tile
+        bool probe = true;
+        if (ch < cnt) {
+            const uint64_t x = __hip_atomic_load(ws.words + (chain + lo + ch) * (4 * kTileChannels) + 3 * kTileChannels,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            probe = (uint32_t)(x >> 32) == ((ch == 0 && lo_incl) ? want_incl : want_agg);
         }
-        if (all) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            break;
+        if (__all(probe)) {
+            bool all = true;
+            const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
+#pragma unroll
+            for (int m = 0; m < MAXT; ++m) {
+                if (m < cnt) {
+                    const uint64_t *src = tiles + m * (4 * kTileChannels) + ch;
+                    const uint32_t want = (m == 0 && lo_incl) ? want_incl : want_agg;
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        w[m][f] = __hip_atomic_load(src + f * kTileChannels, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        all = all && (uint32_t)(w[m][f] >> 32) == want;
+                    }
+                }
+            }
+            if (__all(all)) break;
         }
         ++spins;
         // give up after kMaxSpins, or at once when another wait has already given up
         if (spins > kMaxSpins ||
-            ((spins & 255u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+            ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
             atomicOr(ws.err, 1u);
-            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};  // poison the tile's outputs
+            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
         }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(4);
     }
     St acc = st_empty();
-    float acc_len = 0.f;
 #pragma unroll
-    for (int m = kMaxAnchorGap - 1; m >= 0; --m) {
+    for (int m = 0; m < MAXT; ++m) {
         if (m < cnt) {
-            const int64_t tile = chain + a + m;
-            const uint32_t *src =
-                reinterpret_cast<const uint32_t *>(m == 0 ? ws.incl : ws.agg) + tile * (4 * kTileChannels);
-            float x[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-                x[f] = __uint_as_float(
-                    __hip_atomic_load(src + f * kTileChannels + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            acc = combine(St{x[0], x[1], x[2], x[3]}, acc, acc_len, wc);
-            acc_len += (float)TW;
+            const St x = St{__uint_as_float((uint32_t)w[m][0]), __uint_as_float((uint32_t)w[m][1]),
+                            __uint_as_float((uint32_t)w[m][2]), __uint_as_float((uint32_t)w[m][3])};
+            acc = (m == 0) ? x : combine(acc, x, TW, wc);
         }
     }
     return acc;
 }
 
-template <typename TIn, int MODE>
-constexpr int chunk_max_threads() {
-    return (sizeof(TIn) == 2 && MODE == MODE_PLAIN) ? 1024 : 512;
-}
+// Linear-space fast path of the tile kernel.  Within one wave's L tokens a lane scales every
+// weight by e^{-kmax}, kmax the largest key of its tokens; the weights e^{k_i - kmax} are then
+// at most 1, computed once, and the numerator/denominator run as plain fp32 recurrences
+// (n <- e^w n + X v).  The guard keeps every surviving term a normal fp32 number:
+//   key spread kmax - kmin <= 40 nats and bonus u >= -20, so each current-token weight
+//   e^{u + k_t - kmax} >= e^{-60}, and anything flushed to zero is < 1e-12 of it;
+//   incoming state scale p - kmax <= 60, so it cannot overflow.
+// A lane outside the guard runs the exact per-token max-trick instead (same results within
+// rounding; the tests drive both paths).
+constexpr float kGuardSpread = 40.f;
+constexpr float kGuardBonus = -20.f;
+constexpr float kGuardState = 60.f;
 
-// Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = 16*S tokens),
+// Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = S * L tokens),
 // blockIdx = tt * (B * nCT) + b * nCT + ct, so every tile a workgroup waits for has a
-// lower index and was dispatched earlier.  Thread = (sub-chunk j, channel group g):
-// tid = j * 16 + g, channels ct*64 + 4g .. +3, tokens tt*TW + 16j .. +15.
-// LDS: per sub-chunk and channel the four fields of a state, then the tile's incoming state.
-template <typename TIn, typename TOut, int MODE>
-__global__ void __launch_bounds__((chunk_max_threads<TIn, MODE>()))
-    wkv_chunk_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
-    constexpr int L = kSubLen, G = 16, CW = kTileChannels;
-    using R = typename Raw<TIn>::type;
-    extern __shared__ float smem[];
-    float *sF[4] = {smem, smem + S * CW, smem + 2 * S * CW, smem + 3 * S * CW};
-    float *sI = smem + 4 * S * CW;  // [4][CW]
+// lower index and was dispatched earlier.  Wave w of S = tokens tt*TW + w*L .. +L-1;
+// lane = channel ct*64 + lane.
+//
+// The tile's rows of k, v (and r or x) are staged in LDS as [tensor][TW][64] by 16-byte
+// global-to-LDS loads (global_load_lds_dwordx4): each wave fetches the L rows it computes
+// on, 8 rows of 128 B per instruction, so no VGPR holds a load in flight and a wave waits
+// only for its own rows.  Only the weights X_i stay in VGPRs.  When the pointers are not
+// 16-byte aligned or C is not a multiple of a 16-byte chunk, each lane loads its own
+// channel instead (same LDS layout).  Rows past T and chunks past C read a valid address
+// whose data is never used.  The weights X_i are recomputed from the staged keys in
+// phase E rather than held in VGPRs across the look-back, which keeps the register
+// footprint low enough for every workgroup of a layer-sized call to be resident at once.
+template <typename TIn, typename TOut, int MODE, int L>
+__global__ void __launch_bounds__(1024)
+    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
+    constexpr int CW = kTileChannels;
+    constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    TIn *rows = reinterpret_cast<TIn *>(smem);                                  // [NT][TW][CW]
+    float *sF = reinterpret_cast<float *>(smem + (size_t)NT * TW * CW * sizeof(TIn));  // [4][S][CW]
+    float *sI = sF;  // [4][S][CW] parts of the incoming state, once every wave has read sF
 
-    const int tid = threadIdx.x, g = tid % G, j = tid / G;
+    // wv is the same in every lane of a wave: readfirstlane lets the compiler keep
+    // wave-uniform row and tile addresses in SGPRs
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t BCT = a.B * nCT;
     const int64_t tt = blockIdx.x / BCT;
     const int64_t rem = blockIdx.x - tt * BCT;
     const int64_t b = rem / nCT, ct = rem - b * nCT;
-    const int64_t c0 = ct * CW + g * 4;
-    const int nch = (int)std::max<int64_t>(0, std::min<int64_t>(4, a.C - c0));
+    const int64_t c = ct * CW + lane;
+    const bool cok = c < a.C;
     const int64_t tile_t0 = tt * TW;
     const int64_t tile_len = std::min<int64_t>(TW, a.T - tile_t0);
-    const int64_t t0 = tile_t0 + (int64_t)j * L;
-    const int nval = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - t0));
-    const bool vec = a.vec != 0;
-    const int64_t BC = a.B * a.C, sc = b * a.C + c0;
+    const int64_t t0 = tile_t0 + (int64_t)wv * L;
+    const int wlen = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - t0));  // tokens of this wave
+    const int nval = cok ? wlen : 0;
+    const int64_t C = a.C, BC = a.B * a.C;
+    const int64_t base = (b * a.T + t0) * C + c;
+    const int64_t cs = cok ? c : 0;  // loads stay unpredicated: a lane past C reads channel 0
 
     const TIn *K = static_cast<const TIn *>(a.k);
     const TIn *V = static_cast<const TIn *>(a.v);
     const TIn *GR = static_cast<const TIn *>(MODE == MODE_GATED ? a.r : a.x);
 
-    float w[4], u[4];
-    load_param4(a.w, c0, nch, w);
-    load_param4(a.u, c0, nch, u);
+    // Phase A: stage this wave's rows.
+    {
+        const TIn *src[3] = {K, V, GR};
+        if (a.vec16) {
+            constexpr int CH16 = 16 / (int)sizeof(TIn);  // channels per 16-byte chunk
+            constexpr int CHUNKS = CW / CH16;           // chunks per row: 8 (fp16) or 16 (fp32)
+            constexpr int RPI = 64 / CHUNKS;            // rows per instruction: 8 or 4
+            const int q = lane % CHUNKS, rsub = lane / CHUNKS;
+            int64_t cq = ct * CW + q * CH16;
+            if (cq >= C) cq = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = finite_decay(w[q]);
-
-    // Phase A: every load of the lane's tile slice is issued up front.
-    const int64_t base = (b * a.T + t0) * a.C + c0;
-    R kr[L], vr[L], gr[L];
+            for (int tsr = 0; tsr < NT; ++tsr) {
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const bool ok = i < nval;
-        kr[i] = ok ? load4(K, base + i * a.C, nch, vec) : R{0, 0, 0, 0};
-        vr[i] = ok ? load4(V, base + i * a.C, nch, vec) : R{0, 0, 0, 0};
-        if constexpr (MODE != MODE_PLAIN) gr[i] = ok ? load4(GR, base + i * a.C, nch, vec) : R{0, 0, 0, 0};
-    }
-    R xp = {0, 0, 0, 0};
-    float mk[4], mv[4], mr[4];
-    if constexpr (MODE == MODE_TIMEMIX) {
-        load_param4(a.mix_k, c0, nch, mk);
-        load_param4(a.mix_v, c0, nch, mv);
-        load_param4(a.mix_r, c0, nch, mr);
-        if (nval > 0) {
-            if (t0 > 0)
-                xp = load4(GR, base - a.C, nch, vec);
-            else if (a.x_prev)
-                xp = load4(static_cast<const TIn *>(a.x_prev), sc, nch, vec);
-        }
-    }
-
-    // Phase B: summary of the lane's sub-chunk from the empty state.
-    St sum[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] = st_empty();
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        if (i < nval) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) absorb(sum[q], w[q], (float)kr[i][q], (float)vr[i][q]);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int idx = j * CW + g * 4 + q;
-        sF[0][idx] = sum[q].a;
-        sF[1][idx] = sum[q].b;
-        sF[2][idx] = sum[q].k;
-        sF[3][idx] = sum[q].n;
-    }
-    __syncthreads();
-
-    // Phase C: one lane per channel scans the S summaries (exclusive, from the tile start),
-    // then fetches the tile's incoming state.
-    if (tid < CW) {
-        const int ch = tid;
-        const int64_t c = ct * CW + ch;
-        const bool cok = c < a.C;
-        const float wc = cok ? finite_decay(a.w[c]) : 0.f;
-        St run = st_empty();
-        float run_len = 0.f;
-        for (int jj = 0; jj < S; ++jj) {
-            const int64_t len = std::max<int64_t>(0, std::min<int64_t>(L, a.T - (tile_t0 + (int64_t)jj * L)));
-            const int idx = jj * CW + ch;
-            const St cur = St{sF[0][idx], sF[1][idx], sF[2][idx], sF[3][idx]};
-            sF[0][idx] = run.a;
-            sF[1][idx] = run.b;
-            sF[2][idx] = run.k;
-            sF[3][idx] = run.n;
-            run = combine(run, cur, (float)len, wc);
-            run_len += (float)len;
-        }
-        St prefix = st_empty();
-        if (tt == 0 && a.state_in && cok) {
-            const int64_t s = b * a.C + c;
-            prefix = st_load(a.state_in[s], a.state_in[BC + s], a.state_in[2 * BC + s]);
-        }
-        if (nTT > 1) {
-            const int64_t chain = (b * nCT + ct) * nTT;
-            const bool anchor = (tt % M) == 0, last = tt == nTT - 1;
-            if (!anchor && !last) publish(ws, chain + tt, kAgg, run, ch);
-            if (tt > 0) prefix = lookback(ws, chain, tt, wc, TW, M, ch);
-            if (anchor && !last) publish(ws, chain + tt, kIncl, combine(prefix, run, run_len, wc), ch);
-        }
-        sI[ch] = prefix.a;
-        sI[CW + ch] = prefix.b;
-        sI[2 * CW + ch] = prefix.k;
-        sI[3 * CW + ch] = prefix.n;
-    }
-    __syncthreads();
-
-    // Phase D: the lane's starting state = tile prefix, then the sub-chunks before it.
-    St st[4];
-    const float before = (float)std::min<int64_t>((int64_t)j * L, tile_len);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int cl = g * 4 + q, jl = j * CW + cl;
-        const St pre = St{sI[cl], sI[CW + cl], sI[2 * CW + cl], sI[3 * CW + cl]};
-        const St exl = St{sF[0][jl], sF[1][jl], sF[2][jl], sF[3][jl]};
-        st[q] = combine(pre, exl, before, w[q]);
-    }
-
-    // Phase E: replay the tokens from registers, emit y.
-    TOut *Y = static_cast<TOut *>(a.y);
-    float xs[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xs[q] = (float)xp[q];
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        if (i < nval) {
-            float yv[4], xko[4], xvo[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float kk = (float)kr[i][q], vv = (float)vr[i][q];
-                float num, den;
-                emit(st[q], w[q], u[q], kk, vv, num, den);
-                float gt = 1.f;
-                if constexpr (MODE == MODE_GATED) gt = 1.f + ex(-(float)gr[i][q]);
-                if constexpr (MODE == MODE_TIMEMIX) {
-                    const float xx = (float)gr[i][q];
-                    const float xr = mr[q] * xx + (1.f - mr[q]) * xs[q];
-                    xko[q] = mk[q] * xx + (1.f - mk[q]) * xs[q];
-                    xvo[q] = mv[q] * xx + (1.f - mv[q]) * xs[q];
-                    xs[q] = xx;
-                    gt = 1.f + ex(-xr);
+                for (int j = 0; j < L / RPI; ++j) {
+                    const int r = wv * L + j * RPI;
+                    const int64_t t = std::min<int64_t>(tile_t0 + r + rsub, a.T - 1);
+                    dma16(src[tsr] + (b * a.T + t) * C + cq, rows + ((size_t)tsr * TW + r) * CW);
                 }
-                yv[q] = num * rcp(den * gt);
-                absorb(st[q], w[q], kk, vv);
             }
-            const int64_t off = base + i * a.C;
-            store4(Y, off, nch, vec, yv);
-            if constexpr (MODE == MODE_TIMEMIX) {
-                if (a.xk_out) store4(static_cast<TIn *>(a.xk_out), off, nch, vec, xko);
-                if (a.xv_out) store4(static_cast<TIn *>(a.xv_out), off, nch, vec, xvo);
+        } else {
+            // rolled batches of 4 rows keep this (rare) path's register footprint from
+            // setting the kernel's
+            const int64_t tl = std::min<int64_t>(t0, a.T - 1);
+            const int last = (int)std::min<int64_t>(L - 1, a.T - 1 - tl);
+#pragma unroll
+            for (int tsr = 0; tsr < NT; ++tsr) {
+                const TIn *col = src[tsr] + (b * a.T + tl) * C + cs;
+#pragma unroll 1
+                for (int i0 = 0; i0 < L; i0 += 4) {
+                    TIn tmp[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tmp[i] = col[(int64_t)std::min(i0 + i, last) * C];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rows[((size_t)tsr * TW + wv * L + i0 + i) * CW + lane] = tmp[i];
+                }
             }
         }
+    }
+    // per-channel parameters (and the time-mix token before wave 0's first) load meanwhile
+    const float w_raw = a.w[cs], u_raw = a.u[cs];
+    const float wc = cok ? finite_decay(w_raw) : 0.f;
+    const float uc = cok ? u_raw : 0.f;
+    float xs = 0.f, mr = 0.f, mk = 0.f, mv = 0.f;
+    if constexpr (MODE == MODE_TIMEMIX) {
+        // wave 0: x[tile_t0 - 1] or x_prev (zeros if absent); later waves read it from LDS
+        const bool from_x = tile_t0 > 0, from_prev = tile_t0 == 0 && a.x_prev != nullptr;
+        const TIn *xsrc = from_prev ? static_cast<const TIn *>(a.x_prev) + b * C + cs
+                                    : GR + (from_x ? (b * a.T + tile_t0 - 1) * C + cs : 0);
+        const float xv = (float)*xsrc;
+        const float mr_raw = a.mix_r[cs], mk_raw = a.mix_k[cs], mv_raw = a.mix_v[cs];
+        xs = (from_x || from_prev) ? xv : 0.f;
+        mr = cok ? mr_raw : 0.f;
+        mk = cok ? mk_raw : 0.f;
+        mv = cok ? mv_raw : 0.f;
+    }
+    const float ew = ex(wc), eu = ex(uc);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+    __builtin_amdgcn_wave_barrier();
+
+    const TIn *kr = rows + ((size_t)0 * TW + wv * L) * CW + lane;
+    const TIn *vr = rows + ((size_t)1 * TW + wv * L) * CW + lane;
+    const TIn *gr = rows + ((size_t)2 * TW + wv * L) * CW + lane;
+
+    // Phase B: summary of the wave's tokens from the empty state.  Padded tokens
+    // (i >= nval) get weight X = 0 and decay 1, so they leave every recurrence unchanged.
+    float kmax = -INFINITY, kmin = INFINITY;
+    St sum = st_empty();
+    bool fast;
+    {
+        float xk[L], vb[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            xk[i] = (float)kr[i * CW];
+            vb[i] = (float)vr[i * CW];
+        }
+        if (nval == L) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                kmax = fmaxf(kmax, xk[i]);
+                kmin = fminf(kmin, xk[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                kmax = fmaxf(kmax, i < nval ? xk[i] : -INFINITY);
+                kmin = fminf(kmin, i < nval ? xk[i] : INFINITY);
+            }
+        }
+        fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
+        if (fast) {
+            float nn = 0.f, dd = 0.f;
+            if (nval == L) {
+#pragma unroll
+                for (int i = 0; i < L; ++i) {
+                    const float X = ex(xk[i] - kmax);
+                    nn = fmaf(ew, nn, X * vb[i]);
+                    dd = fmaf(ew, dd, X);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < L; ++i) {
+                    const float X = (i < nval) ? ex(xk[i] - kmax) : 0.f;
+                    const float e = (i < nval) ? ew : 1.f;
+                    nn = fmaf(e, nn, X * vb[i]);
+                    dd = fmaf(e, dd, X);
+                }
+            }
+            sum = St{nn, dd, kmax, 0.f};
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i)
+                if (i < nval) absorb(sum, wc, xk[i], vb[i]);
+        }
+    }
+    sF[(0 * S + wv) * CW + lane] = sum.a;
+    sF[(1 * S + wv) * CW + lane] = sum.b;
+    sF[(2 * S + wv) * CW + lane] = sum.k;
+    sF[(3 * S + wv) * CW + lane] = sum.n;
+    __syncthreads();
+
+    // Phase C: each wave folds the summaries of the waves before it (fixed order); the last
+    // wave forms the tile aggregate and publishes it.
+    St excl = st_empty();
+    for (int j = 0; j < wv; ++j) {
+        const St sj = St{sF[(0 * S + j) * CW + lane], sF[(1 * S + j) * CW + lane],
+                         sF[(2 * S + j) * CW + lane], sF[(3 * S + j) * CW + lane]};
+        const int lj = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - (tile_t0 + (int64_t)j * L)));
+        excl = combine(excl, sj, (float)lj, wc);
+    }
+    const int64_t chain = (b * nCT + ct) * nTT;
+    const bool anchor = (tt % M) == 0, last = tt == nTT - 1;
+    St agg = st_empty();
+    if (wv == S - 1) {
+        agg = combine(excl, sum, (float)wlen, wc);
+        if (nTT > 1 && !anchor && !last) publish(ws, chain + tt, kAgg, agg, lane);
+    }
+
+    // Phase D: the tile's incoming state.  Anchor tiles (every M-th, tile 0 included) publish
+    // their inclusive state, the others only their aggregate; with a the last anchor before tt
+    // the prefix is INCL(a) + AGG(a+1) + ... + AGG(tt-1), folded in that fixed order whatever
+    // the timing, so results are bitwise reproducible.  The waves share the polling: wave w
+    // folds a contiguous part, then every wave folds the parts in order.
+    St prefix = st_empty();
+    if (tt == 0) {
+        if (a.state_in && cok)
+            prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
+    } else {
+        const int a0 = (int)(((tt - 1) / M) * M);
+        const int cnt = (int)tt - a0;
+        const int q = (cnt + S - 1) / S;
+        const int lo = a0 + wv * q, hi = std::min(lo + q, (int)tt);
+        St part = st_empty();
+        if (lo < hi) part = fold_published<kMaxAnchorGap / 4>(ws, chain, lo, hi, lo == a0, wc, (float)TW, lane);
+        __syncthreads();  // sI reuses sF: every wave has folded its summaries (phase C)
+        sI[(0 * S + wv) * CW + lane] = part.a;
+        sI[(1 * S + wv) * CW + lane] = part.b;
+        sI[(2 * S + wv) * CW + lane] = part.k;
+        sI[(3 * S + wv) * CW + lane] = part.n;
+        __syncthreads();
+        for (int j = 0; j < S; ++j) {
+            const int lj = a0 + j * q;
+            if (lj < (int)tt) {
+                const St pj = St{sI[(0 * S + j) * CW + lane], sI[(1 * S + j) * CW + lane],
+                                 sI[(2 * S + j) * CW + lane], sI[(3 * S + j) * CW + lane]};
+                const float span = (float)((std::min(lj + q, (int)tt) - lj) * TW);
+                prefix = (j == 0) ? pj : combine(prefix, pj, span, wc);
+            }
+        }
+    }
+    if (wv == S - 1 && nTT > 1 && anchor && !last)
+        publish(ws, chain + tt, kIncl, combine(prefix, agg, (float)tile_len, wc), lane);
+    const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
+
+    // Phase E: emit y for the wave's tokens, starting from st.
+    TOut *Y = static_cast<TOut *>(a.y);
+    TIn *XKO = static_cast<TIn *>(a.xk_out);
+    TIn *XVO = static_cast<TIn *>(a.xv_out);
+    if constexpr (MODE == MODE_TIMEMIX) {
+        if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
+    }
+    // gate argument in base 2: -log2(e) * (mr x + (1 - mr) xs)
+    const float ga = -kLog2e * mr, gb = -kLog2e * (1.f - mr);
+    const float pst = st_logmax(st, wc);
+    St fin;
+    if (fast && pst - kmax <= kGuardState) {
+        const float s0 = ex(pst - kmax);
+        float nn = st.a * s0, dd = st.b * s0;
+        // rows as wave-uniform pointers plus a 32-bit lane offset
+        const int64_t row0 = (b * a.T + t0) * C + ct * CW;
+        const unsigned Cu = (unsigned)C;
+        // a full wave (all L tokens, all 64 channels in range) stages y in its own v rows,
+        // dead once v is in registers, and writes 16 bytes per lane
+        constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
+        const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16;
+        TOut *ystage = reinterpret_cast<TOut *>(rows + ((size_t)1 * TW + wv * L) * CW);
+        // the rows are read from LDS in batches of LB to bound the registers they occupy
+        constexpr int LB = 8;
+        if (nval == L) {
+#pragma unroll
+            for (int h = 0; h < L; h += LB) {
+                float xk[LB], ve[LB], ge[LB];
+#pragma unroll
+                for (int j = 0; j < LB; ++j) {
+                    xk[j] = (float)kr[(h + j) * CW];
+                    ve[j] = (float)vr[(h + j) * CW];
+                    ge[j] = (MODE == MODE_PLAIN) ? 0.f : (float)gr[(h + j) * CW];
+                }
+#pragma unroll
+                for (int j = 0; j < LB; ++j) {
+                    const int i = h + j;
+                    const float X = ex(xk[j] - kmax), vv = ve[j];  // the weight X_i
+                    const float XU = X * eu;
+                    const float num = fmaf(XU, vv, nn);
+                    const float den = dd + XU;
+                    float g = 1.f;
+                    const unsigned off = i * Cu + (unsigned)lane;
+                    if constexpr (MODE == MODE_GATED) g = 1.f + __builtin_amdgcn_exp2f(-kLog2e * ge[j]);
+                    if constexpr (MODE == MODE_TIMEMIX) {
+                        const float xx = ge[j];
+                        g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
+                        if (XKO) (XKO + row0)[off] = (TIn)fmaf(mk, xx - xs, xs);
+                        if (XVO) (XVO + row0)[off] = (TIn)fmaf(mv, xx - xs, xs);
+                        xs = xx;
+                    }
+                    const TOut yv = (TOut)(num * rcp(den * g));
+                    if (stage_y)
+                        ystage[i * CW + lane] = yv;
+                    else
+                        (Y + row0)[off] = yv;
+                    nn = fmaf(ew, nn, X * vv);
+                    dd = fmaf(ew, dd, X);
+                }
+            }
+            if constexpr (kStageFits) {
+                if (stage_y) {
+                    __builtin_amdgcn_wave_barrier();
+                    constexpr int CH16 = 16 / (int)sizeof(TOut);  // outputs per 16-byte chunk
+                    constexpr int CHUNKS = CW / CH16;
+                    constexpr int RPI = 64 / CHUNKS;             // rows per store instruction
+                    const int q = lane % CHUNKS, rs = lane / CHUNKS;
+#pragma unroll
+                    for (int j = 0; j < L / RPI; ++j) {
+                        const int r = j * RPI + rs;
+                        const f4 chunk = *reinterpret_cast<const f4 *>(ystage + r * CW + q * CH16);
+                        *reinterpret_cast<f4 *>(Y + row0 + (int64_t)r * C + q * CH16) = chunk;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const float kk = (float)kr[i * CW], vv = (float)vr[i * CW];
+                const float X = (i < nval) ? ex(kk - kmax) : 0.f;
+                const float XU = X * eu;
+                const float num = fmaf(XU, vv, nn);
+                const float den = dd + XU;
+                float g = 1.f;
+                float xx = 0.f;
+                if constexpr (MODE == MODE_GATED) g = 1.f + __builtin_amdgcn_exp2f(-kLog2e * (float)gr[i * CW]);
+                if constexpr (MODE == MODE_TIMEMIX) {
+                    xx = (float)gr[i * CW];
+                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
+                }
+                const float yv = num * rcp(den * g);
+                if (i < nval) {
+                    Y[base + i * C] = (TOut)yv;
+                    if constexpr (MODE == MODE_TIMEMIX) {
+                        if (XKO) XKO[base + i * C] = (TIn)fmaf(mk, xx - xs, xs);
+                        if (XVO) XVO[base + i * C] = (TIn)fmaf(mv, xx - xs, xs);
+                    }
+                }
+                if constexpr (MODE == MODE_TIMEMIX) xs = (i < nval) ? xx : xs;
+                const float e = (i < nval) ? ew : 1.f;
+                nn = fmaf(e, nn, X * vv);
+                dd = fmaf(e, dd, X);
+            }
+        }
+        fin = St{nn, dd, kmax, 0.f};
+    } else {
+        // exact per-token max-trick
+        St s2 = st;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if (i < nval) {
+                const float kk = (float)kr[i * CW];
+                const float vv = (float)vr[i * CW];
+                float num, den;
+                emit(s2, wc, uc, kk, vv, num, den);
+                float g = 1.f;
+                if constexpr (MODE == MODE_GATED) g = 1.f + ex(-(float)gr[i * CW]);
+                if constexpr (MODE == MODE_TIMEMIX) {
+                    const float xx = (float)gr[i * CW];
+                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
+                    if (XKO) XKO[base + i * C] = (TIn)fmaf(mk, xx - xs, xs);
+                    if (XVO) XVO[base + i * C] = (TIn)fmaf(mv, xx - xs, xs);
+                    xs = xx;
+                }
+                Y[base + i * C] = (TOut)(num * rcp(den * g));
+                absorb(s2, wc, kk, vv);
+            }
+        }
+        fin = s2;
     }
 
     // Phase F: the lane holding token T-1 writes the final state (and x_last).
     if (nval > 0 && t0 + nval == a.T) {
         if (a.state_out) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (q < nch) {
-                    a.state_out[sc + q] = st[q].a;
-                    a.state_out[BC + sc + q] = st[q].b;
-                    a.state_out[2 * BC + sc + q] = st_logmax(st[q], w[q]);
-                }
+            a.state_out[b * C + c] = fin.a;
+            a.state_out[BC + b * C + c] = fin.b;
+            a.state_out[2 * BC + b * C + c] = st_logmax(fin, wc);
         }
         if constexpr (MODE == MODE_TIMEMIX) {
-            if (a.x_last) store4(static_cast<TIn *>(a.x_last), sc, nch, vec, xs);
+            if (a.x_last) static_cast<TIn *>(a.x_last)[b * C + c] = (TIn)xs;
         }
     }
 }
@@ -527,21 +735,30 @@ hipError_t launch_seq_t(const ForwardArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int MODE>
-hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
-                          hipStream_t s) {
-    const int S = chunk_len / kSubLen;
+template <typename TIn, typename TOut, int MODE, int L>
+hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    const int S = chunk_len / L;
     const int nCT = (int)((a.C + kTileChannels - 1) / kTileChannels);
     const int nTT = (int)((a.T + chunk_len - 1) / chunk_len);
     const int64_t blocks = a.B * (int64_t)nCT * nTT;
-    const size_t lds = (size_t)(4 * S * kTileChannels + 4 * kTileChannels) * sizeof(float);
-    if (blocks > 0x7fffffff || 16 * S > chunk_max_threads<TIn, MODE>()) return hipErrorInvalidConfiguration;
-    // anchor spacing ~ sqrt(tiles per chain): the anchor chain and each tile's fold stay short
-    int M = 4;
-    while (M < kMaxAnchorGap && (int64_t)M * M < nTT) M <<= 1;
-    hipLaunchKernelGGL((wkv_chunk_kernel<TIn, TOut, MODE>), dim3((unsigned)blocks), dim3(16 * S), lds,
-                       s, a, ws, S, nCT, nTT, chunk_len, M);
+    constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;
+    // staged rows + wave summaries (later the parts of the incoming state).  28 KB for the
+    // fp16 time-mix at 64 tokens: LDS is allocated in granules that make 32 KB fit only 4
+    // workgroups per CU (160 KB), 28 KB five.
+    const size_t lds = (size_t)NT * chunk_len * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
+    if (lds > 65536) return hipErrorInvalidConfiguration;
+    if (blocks > 0x7fffffff || S < 1 || 64 * S > 1024) return hipErrorInvalidConfiguration;
+    // an anchor every 16 tiles: a chain of up to 16 tiles has no serial anchor hop at all
+    const int M = kMaxAnchorGap;
+    if (S < 4) return hipErrorInvalidConfiguration;  // each wave polls at most 16 / S tiles
+    hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, L>), dim3((unsigned)blocks), dim3(64 * S), lds, s, a,
+                       ws, S, nCT, nTT, chunk_len, M);
     return hipGetLastError();
+}
+
+template <typename TIn, typename TOut, int MODE>
+hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    return launch_tile<TIn, TOut, MODE, 16>(a, chunk_len, ws, s);
 }
 
 #define RWKV_DISPATCH(LAUNCH, ...)                                                              \
@@ -568,7 +785,11 @@ hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorksp
 
 }  // namespace
 
-int chunk_max_len(int in_f16, int mode) { return (in_f16 && mode == MODE_PLAIN) ? 1024 : 512; }
+// Longest tile per dtype: the tile's rows are staged in LDS (64 KB per workgroup).
+int chunk_max_len(int in_f16, int mode) {
+    (void)mode;
+    return in_f16 ? 128 : 64;
+}
 
 bool auto_sequential(int64_t B, int64_t T, int64_t C) {
     // Enough independent (b, channel) lanes to fill every SIMD twice over: the
@@ -580,18 +801,17 @@ bool auto_sequential(int64_t B, int64_t T, int64_t C) {
 int auto_chunk_len(int64_t B, int64_t T, int64_t C) {
     (void)B;
     (void)C;
-    int len = kMinChunk;
-    while (len < 256 && (int64_t)len * 4 < T) len <<= 1;
-    return len;
+    (void)T;
+    // 64-token tiles (4 waves of 16 tokens): the most workgroups per chain, short in-tile scans
+    return kMinChunk;
 }
 
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
     const int64_t nCT = (C + kTileChannels - 1) / kTileChannels;
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
-    // flags [tiles][64] u32 + agg, incl [tiles][4][64] f32 + one error word, 256-B aligned parts
-    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-    return (size_t)(al(tiles * kTileChannels * 4) + 2 * al(tiles * 4 * kTileChannels * 4) + 256);
+    // words [tiles][4][64] u64 (one published state per tile) + one error word
+    return (size_t)(tiles * 4 * kTileChannels * 8 + 256);
 }
 
 void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
@@ -599,15 +819,9 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
     const int64_t nCT = (C + kTileChannels - 1) / kTileChannels;
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
-    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
     char *p = static_cast<char *>(base);
-    ws->flags = reinterpret_cast<uint32_t *>(p);
-    p += al(tiles * kTileChannels * 4);
-    ws->agg = reinterpret_cast<float *>(p);
-    p += al(tiles * 4 * kTileChannels * 4);
-    ws->incl = reinterpret_cast<float *>(p);
-    p += al(tiles * 4 * kTileChannels * 4);
-    ws->err = reinterpret_cast<uint32_t *>(p);
+    ws->words = reinterpret_cast<uint64_t *>(p);
+    ws->err = reinterpret_cast<uint32_t *>(p + tiles * 4 * kTileChannels * 8);
 }
 
 hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATCH(launch_seq_t, a, s); }

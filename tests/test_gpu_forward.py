@@ -44,8 +44,7 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
     return host(y), (host(so) if so is not None else None)
 
 
-ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("chunked", 256), ("chunked", 512),
-         ("auto", 0)]
+ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("auto", 0)]
 
 
 # ----------------------------------------------------------------------------- small, ragged
@@ -54,6 +53,8 @@ ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("chunked", 256),
 @pytest.mark.parametrize("algo,chunk", ALGOS)
 def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64
+    if in_dt == "f32" and chunk > 64:
+        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
     case = wi.forward_case(2, 1000, 200, seed=41, in_dtype=in_dt, out_dtype=out_dt, gated=True, prior=True)
     ref = oracle_forward(("ragged", in_dt), case)
     y, st = run(case, algo, chunk, label="ragged")
@@ -63,7 +64,7 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 256)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128)])
 def test_odd_channels(C, algo, chunk):
     # C % 4 != 0 takes the per-element path; C < 64 leaves most of a tile masked
     case = wi.forward_case(3, 300, C, seed=42, in_dtype="f16", gated=True, prior=True)
@@ -132,7 +133,7 @@ def test_state_in_place_and_null_state():
     t = torch()
     case = wi.forward_case(2, 700, 128, seed=46, in_dtype="f16", gated=True, prior=True)
     ref = oracle_forward("inplace", case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 128)):
         st = to_dev(case["state_in"])
         y = t.empty((2, 700, 128), dtype=t.float16, device="cuda:0")
         note(f"forward in-place state {algo}/{chunk}")
@@ -154,7 +155,7 @@ def test_full_forgetting_channels():
     case["w"] = case["w"].copy()
     case["w"][::3] = -np.inf
     ref = oracle.forward(case, method="direct")
-    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64)):
         y, st = run(case, algo, chunk, label="w=-inf")
         check_output(y, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
         check_state(st, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
@@ -170,7 +171,7 @@ def test_shift_invariance_needs_max_trick(shift):
     st[2] = st[2] + shift
     case["state_in"] = st
     ref = oracle.forward(case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 512)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64)):
         y, s = run(case, algo, chunk, label=f"shift {shift}")
         check_output(y, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
         check_state(s, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
@@ -182,7 +183,7 @@ def test_wide_key_spread():
     g = np.random.default_rng(49)
     case["k"] = g.uniform(-60, 60, case["k"].shape).astype(np.float32)
     ref = oracle.forward(case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 256)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64)):
         y, s = run(case, algo, chunk, label="wide spread")
         check_output(y, ref, TOL["f32"], f"spread {algo}/{chunk}")
         check_state(s, ref, TOL["f32"], f"spread {algo}/{chunk}")
@@ -201,7 +202,7 @@ def test_split_sequence_carry():
     y1 = rw.rwkv4_wkv_forward(dk[:, :T1].contiguous(), dv[:, :T1].contiguous(), w, u, state_in=st,
                               state_out=st, r=dr[:, :T1].contiguous(), algo="chunked", chunk_len=64)
     y2 = rw.rwkv4_wkv_forward(dk[:, T1:].contiguous(), dv[:, T1:].contiguous(), w, u, state_in=st,
-                              state_out=st, r=dr[:, T1:].contiguous(), algo="chunked", chunk_len=128)
+                              state_out=st, r=dr[:, T1:].contiguous(), algo="chunked", chunk_len=64)
     t.cuda.synchronize()
     y = np.concatenate([host(y1), host(y2)], axis=1)
     check_output(y, ref, TOL["f32"], "split carry")
@@ -230,7 +231,7 @@ def test_negative_controls_fail_the_gate():
     from oracle import compare as cmp
     case = wi.forward_case(2, 512, 128, seed=52, in_dtype="f32", gated=True, prior=True)
     ref = oracle.forward(case)
-    y, _ = run(case, "chunked", 128, label="negative controls")
+    y, _ = run(case, "chunked", 64, label="negative controls")
     tol = TOL["f32"]
     assert cmp.scaled_error(y, ref["y"], ref["scale"]) <= tol
     g = 1.0 / (1.0 + np.exp(-case["r"].astype(np.float64)))
@@ -249,7 +250,7 @@ def test_negative_controls_fail_the_gate():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("algo,chunk", ALGOS)
+@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[1] <= 64])
 def test_workload_169m_fp32(algo, chunk):
     """B1 T1024 C768, fp32 k, v ~ N(0,1), empty state, y = wkv (fp32): bar 1e-5."""
     case = wi.workload_inputs(0)

@@ -29,7 +29,7 @@ def inputs():
     return _cache["case"], _cache["ref"], _cache["dev"]
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 256, 512, 1024, 0])
+@pytest.mark.parametrize("chunk", [64, 128, 0])
 def test_long_sequence_chunk_sweep(chunk):
     import rwkv_wkv_linear_amd as rw
     t = torch()

@@ -60,7 +60,7 @@ def check_all(out, ref, case, what, with_xkv):
             note(f"{what}: {name} max |err| - bound = {excess:.3e}")
             assert excess <= 0, f"{what}: {name} off by more than half an ulp"
 
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 256), ("chunked", 512)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128)])
 @pytest.mark.parametrize("with_xkv", [False, True])
 def test_ragged_prior(algo, chunk, with_xkv):
     case = wi.timemix_case(2, 777, 136, seed=61, prior=True)
@@ -96,8 +96,7 @@ def test_zero_tokens():
     assert np.array_equal(host(so), case["state_in"].astype(np.float64))
 
 
-@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("sequential", 0), ("chunked", 64), ("chunked", 128),
-                                        ("chunked", 256), ("chunked", 512)])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("sequential", 0), ("chunked", 64), ("chunked", 128)])
 def test_workload_14b_layer(algo, chunk):
     """B1 T1024 C5120 fp16, token shift from x_prev, r = xr, y = sigmoid(xr) wkv (fp16)."""
     case = wi.workload_inputs(2)
