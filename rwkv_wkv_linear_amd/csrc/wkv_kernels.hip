@@ -266,52 +266,58 @@ __device__ __forceinline__ void publish(const ChunkWorkspace &ws, int64_t tile, 
 }
 
 // Fold of the published states of tiles [lo, hi) of a chain, left to right; tile lo is an
-// anchor (inclusive state) when lo_incl is set, every other tile an aggregate.  Waiting
-// costs one word per tile: lane m polls the last field of channel 0 of tile lo + m, with a
-// back-off, until the wave sees them all tagged; then every lane loads its channel's fields
-// and checks every tag (a word written by the same store instruction for another channel may
-// become visible a little later; that case polls again).  Returns NaNs if the wait gives up
-// (then the failure shows in the outputs and ws.err is set).
+// anchor (inclusive state) when lo_incl is set, every other tile an aggregate.  Every lane
+// loads its channel's fields of every tile and checks every tag.  While some are missing the
+// wave waits on one word per tile (lane m polls the last field of channel 0 of tile lo + m,
+// with a back-off) before reading everything again (a word written by the same store
+// instruction for another channel may become visible a little later than the polled one).
+// Returns NaNs if the wait gives up (then the failure shows in the outputs and ws.err is set).
 template <int MAXT>
 __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo, int64_t hi, bool lo_incl,
                              float wc, float TW, int ch) {
     const int cnt = (int)(hi - lo);
     const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
     uint64_t w[MAXT][4];
-    uint32_t spins = 0;
-    for (;;) {
-        // cheap readiness probe: one word per tile
-        bool probe = true;
-        if (ch < cnt) {
-            const uint64_t x = __hip_atomic_load(ws.words + (chain + lo + ch) * (4 * kTileChannels) + 3 * kTileChannels,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            probe = (uint32_t)(x >> 32) == ((ch == 0 && lo_incl) ? want_incl : want_agg);
-        }
-        if (__all(probe)) {
-            bool all = true;
-            const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
+    const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
+    // One attempt reads every word.  The predecessors have usually published by the time a
+    // tile gets here, so the first attempt normally succeeds in a single memory round trip;
+    // otherwise a cheap probe (one word per tile) spins until all look ready, and the full
+    // read repeats.
+    auto read_all = [&]() -> bool {
+        bool all = true;
 #pragma unroll
-            for (int m = 0; m < MAXT; ++m) {
-                if (m < cnt) {
-                    const uint64_t *src = tiles + m * (4 * kTileChannels) + ch;
-                    const uint32_t want = (m == 0 && lo_incl) ? want_incl : want_agg;
+        for (int m = 0; m < MAXT; ++m) {
+            if (m < cnt) {
+                const uint64_t *src = tiles + m * (4 * kTileChannels) + ch;
+                const uint32_t want = (m == 0 && lo_incl) ? want_incl : want_agg;
 #pragma unroll
-                    for (int f = 0; f < 4; ++f) {
-                        w[m][f] = __hip_atomic_load(src + f * kTileChannels, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        all = all && (uint32_t)(w[m][f] >> 32) == want;
-                    }
+                for (int f = 0; f < 4; ++f) {
+                    w[m][f] = __hip_atomic_load(src + f * kTileChannels, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && (uint32_t)(w[m][f] >> 32) == want;
                 }
             }
-            if (__all(all)) break;
         }
-        ++spins;
-        // give up after kMaxSpins, or at once when another wait has already given up
-        if (spins > kMaxSpins ||
-            ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-            atomicOr(ws.err, 1u);
-            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
+        return __all(all);
+    };
+    uint32_t spins = 0;
+    while (!read_all()) {
+        for (;;) {
+            ++spins;
+            // give up after kMaxSpins, or at once when another wait has already given up
+            if (spins > kMaxSpins ||
+                ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+                atomicOr(ws.err, 1u);
+                return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
+            }
+            __builtin_amdgcn_s_sleep(4);
+            bool probe = true;
+            if (ch < cnt) {
+                const uint64_t x = __hip_atomic_load(tiles + ch * (4 * kTileChannels) + 3 * kTileChannels,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                probe = (uint32_t)(x >> 32) == ((ch == 0 && lo_incl) ? want_incl : want_agg);
+            }
+            if (__all(probe)) break;
         }
-        __builtin_amdgcn_s_sleep(4);
     }
     St acc = st_empty();
 #pragma unroll
@@ -337,6 +343,64 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 constexpr float kGuardSpread = 40.f;
 constexpr float kGuardBonus = -20.f;
 constexpr float kGuardState = 60.f;
+
+// Linear-space emit of one wave's L tokens when all of them are valid: y_i from the running
+// numerator/denominator (nn, dd, scaled by e^{-kmax}), then the recurrence step.  With
+// P = X v the four updates are single FMAs: num = nn + e^u P, den = dd + e^u X,
+// nn <- e^w nn + P, dd <- e^w dd + X.  The optional writes are template switches so the
+// unrolled loop has no branches: STAGE puts y in the wave's LDS v rows (each row is read
+// into registers before it is overwritten; the caller then writes 16 bytes per lane), MIX
+// writes the time-mix xk/xv rows.  kr, vr, gr point at the lane's first staged row.
+template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
+__device__ __forceinline__ void emit_full(const TIn *kr, const TIn *vr, const TIn *gr, float kmax, float eu,
+                                          float ew, float ga, float gb, float mk, float mv, float &xs, float &nn,
+                                          float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
+                                          unsigned Cu, int lane) {
+    constexpr int CW = kTileChannels;
+    constexpr int LB = 8;  // rows read from LDS per batch, to bound the registers they occupy
+    // products with a +0 addend keep fp16 operands in a mixed-precision FMA (no separate
+    // conversion); they round exactly like the plain product
+    float gbx = gb * xs;  // the gate's previous-token term
+#pragma unroll
+    for (int h = 0; h < L; h += LB) {
+        TIn kh[LB], vh[LB], gh[LB];
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+            kh[j] = kr[(h + j) * CW];
+            vh[j] = vr[(h + j) * CW];
+            gh[j] = (MODE == MODE_PLAIN) ? TIn(0) : gr[(h + j) * CW];
+        }
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+            const int i = h + j;
+            const float X = ex((float)kh[j] - kmax);  // e^{k_i - kmax}, subtracted first: exact for large keys
+            const float P = fmaf(X, (float)vh[j], 0.f);
+            const float num = fmaf(eu, P, nn);
+            const float den = fmaf(eu, X, dd);
+            float dg = den;  // den * (1 + e^{-r})
+            if constexpr (MODE == MODE_GATED) dg = fmaf(den, __builtin_amdgcn_exp2f(-kLog2e * (float)gh[j]), den);
+            if constexpr (MODE == MODE_TIMEMIX) {
+                dg = fmaf(den, __builtin_amdgcn_exp2f(fmaf(ga, (float)gh[j], gbx)), den);
+                if constexpr (MIX) {
+                    const float xx = (float)gh[j];
+                    const unsigned off = i * Cu + (unsigned)lane;
+                    if (xkrow) xkrow[off] = (TIn)fmaf(mk, xx - xs, xs);
+                    if (xvrow) xvrow[off] = (TIn)fmaf(mv, xx - xs, xs);
+                    xs = xx;
+                }
+                gbx = fmaf(gb, (float)gh[j], 0.f);
+            }
+            const TOut yv = (TOut)(num * rcp(dg));
+            if constexpr (STAGE)
+                ystage[i * CW + lane] = yv;
+            else
+                yrow[i * Cu + (unsigned)lane] = yv;
+            nn = fmaf(ew, nn, P);
+            dd = fmaf(ew, dd, X);
+        }
+    }
+    if constexpr (MODE == MODE_TIMEMIX && !MIX) xs = (float)gr[(L - 1) * CW];
+}
 
 // Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = S * L tokens),
 // blockIdx = tt * (B * nCT) + b * nCT + ct, so every tile a workgroup waits for has a
@@ -579,44 +643,23 @@ __global__ void __launch_bounds__(1024)
         constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
         const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16;
         TOut *ystage = reinterpret_cast<TOut *>(rows + ((size_t)1 * TW + wv * L) * CW);
-        // the rows are read from LDS in batches of LB to bound the registers they occupy
-        constexpr int LB = 8;
         if (nval == L) {
-#pragma unroll
-            for (int h = 0; h < L; h += LB) {
-                float xk[LB], ve[LB], ge[LB];
-#pragma unroll
-                for (int j = 0; j < LB; ++j) {
-                    xk[j] = (float)kr[(h + j) * CW];
-                    ve[j] = (float)vr[(h + j) * CW];
-                    ge[j] = (MODE == MODE_PLAIN) ? 0.f : (float)gr[(h + j) * CW];
+            const bool mix = (MODE == MODE_TIMEMIX) && (XKO || XVO);
+            TOut *yrow = Y + row0;
+            TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
+#define RWKV_EMIT(STAGE, MIX)                                                                          \
+    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(kr, vr, gr, kmax, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
+                                              xkrow, xvrow, ystage, Cu, lane)
+            if constexpr (MODE == MODE_TIMEMIX) {
+                if (stage_y) {
+                    if (mix) RWKV_EMIT(true, true); else RWKV_EMIT(true, false);
+                } else {
+                    if (mix) RWKV_EMIT(false, true); else RWKV_EMIT(false, false);
                 }
-#pragma unroll
-                for (int j = 0; j < LB; ++j) {
-                    const int i = h + j;
-                    const float X = ex(xk[j] - kmax), vv = ve[j];  // the weight X_i
-                    const float XU = X * eu;
-                    const float num = fmaf(XU, vv, nn);
-                    const float den = dd + XU;
-                    float g = 1.f;
-                    const unsigned off = i * Cu + (unsigned)lane;
-                    if constexpr (MODE == MODE_GATED) g = 1.f + __builtin_amdgcn_exp2f(-kLog2e * ge[j]);
-                    if constexpr (MODE == MODE_TIMEMIX) {
-                        const float xx = ge[j];
-                        g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
-                        if (XKO) (XKO + row0)[off] = (TIn)fmaf(mk, xx - xs, xs);
-                        if (XVO) (XVO + row0)[off] = (TIn)fmaf(mv, xx - xs, xs);
-                        xs = xx;
-                    }
-                    const TOut yv = (TOut)(num * rcp(den * g));
-                    if (stage_y)
-                        ystage[i * CW + lane] = yv;
-                    else
-                        (Y + row0)[off] = yv;
-                    nn = fmaf(ew, nn, X * vv);
-                    dd = fmaf(ew, dd, X);
-                }
+            } else {
+                if (stage_y) RWKV_EMIT(true, false); else RWKV_EMIT(false, false);
             }
+#undef RWKV_EMIT
             if constexpr (kStageFits) {
                 if (stage_y) {
                     __builtin_amdgcn_wave_barrier();
