@@ -1,21 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the RWKV-4 WKV time-mixing hot path on one MI355X.
 
-Workload (one "step" = one call of rwkv4_timemix_fused, i.e. the whole path: token
-shift -> r = xr -> WKV recurrence with fp32 state -> sigmoid gate -> y, plus the
+Default workload (one "step" = one call of rwkv4_timemix_fused, i.e. the whole path:
+token shift -> r = xr -> WKV recurrence with fp32 state -> sigmoid gate -> y, plus the
 final state and x_last): the RWKV-4 14B layer shape B1 T1024 C5120 with fp16
 activations, x ~ N(0,1), x_prev ~ N(0,1), mix_* ~ U(0,1), k, v ~ N(0,1), decay and
-bonus by the workload recipe, empty prior state.  Inputs are resident in HBM when
-the timed region starts; each step uses the next of R rotated buffer sets (>= 1.25
-GiB in total), so the 256 MB Infinity Cache cannot serve a step's inputs from an
-earlier step.
+bonus by the workload recipe, empty prior state.  Inputs are resident in HBM when the
+timed region starts; each step uses the next of R rotated buffer sets (>= 1.25 GiB in
+total), so the 256 MB Infinity Cache cannot serve a step's inputs from an earlier step.
 
-Prints ONE JSON line: throughput in tokens*channels/s (B*T*C per step over the
-wall time of the K timed steps), the roofline of the kernel (algorithmic bytes per
-launch over its average duration: a pair of HIP events on the kernel's stream brackets
-the K back-to-back launches), and the fp64 CPU oracle timed on the host cores.
+Prints ONE JSON line: throughput in tokens*channels/s (B*T*C per step over the wall
+time of the K timed steps), the roofline of the kernel (algorithmic bytes per launch
+over its average duration: a pair of HIP events on the kernel's stream brackets the
+K back-to-back launches), and the fp64 CPU oracle timed on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--chunk-len L] [--algo auto|chunked|sequential]
+--workload selects one of the other shapes the library is tested on (same fields):
+  plain169m  rwkv4_wkv_forward  B1 T1024 C768, fp32 in/out, ungated
+  gated169m  rwkv4_wkv_forward  B8 T1024 C768, fp16 in/out, gated, prior state
+  decode14b  40 x rwkv4_wkv_step  B256 C5120, fp16, gated, state in place (a step = 40 layers)
+  long       rwkv4_wkv_forward  B1 T65536 C2048, fp16 in, fp32 out
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chunk-len L] [--algo A]
     python bench.py --copy-kernel      # plain device copy, for counter calibration
 """
 from __future__ import annotations
@@ -37,14 +42,24 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "timemix_14b_layer_counters.txt")
 KERNEL_SRC = os.path.join(ROOT, "rwkv_wkv_linear_amd", "csrc", "wkv_kernels.hip")
-WORKLOAD = "rwkv4-14b time-mix fused prefill B1 T1024 C5120 (fp16 I/O)"
+
+# name -> (workload index in wkv_inputs.WORKLOADS, description)
+WORKLOADS = {
+    "timemix14b": (2, "rwkv4-14b time-mix fused prefill B1 T1024 C5120 (fp16 I/O)"),
+    "plain169m": (0, "rwkv4-169m wkv forward B1 T1024 C768 (fp32 I/O, ungated)"),
+    "gated169m": (1, "rwkv4-169m gated prefill B8 T1024 C768 (fp16 I/O, prior state)"),
+    "decode14b": (3, "rwkv4-14b batched decode, 40 layers x B256 C5120 (fp16 I/O, state in place)"),
+    "long": (4, "long-sequence forward B1 T65536 C2048 (fp16 in, fp32 out)"),
+}
+CPU_BUDGET_S = 10.0  # CPU seconds the oracle leg spends (at least 3 runs)
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default by workload)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="timemix14b", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "sequential"])
     ap.add_argument("--rotate-gib", type=float, default=1.25)
@@ -71,7 +86,7 @@ def counters_traffic():
     fields = {}
     with open(COUNTERS_FILE) as f:
         for line in f:
-            if ":" in line:
+            if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
     with open(KERNEL_SRC, "rb") as f:
@@ -84,24 +99,25 @@ def counters_traffic():
         return None
 
 
-def cpu_baseline(case, B, T, C):
-    """The fp64 oracle as it stands (token shift + linear-space recurrence + final state)
-    on the full workload; median of repeated runs, at least 3, about 3 s in all."""
+def cpu_baseline(name, case, elements, sample):
+    """The fp64 oracle as it stands, on the host cores: median of repeated runs over
+    `case` (at least 3, about CPU_BUDGET_S seconds in all)."""
     import oracle
+    run = {"timemix14b": oracle.timemix, "decode14b": lambda c: [oracle.step(l) for l in c]}.get(
+        name, oracle.forward)
     times = []
-    t_end = time.perf_counter() + 3.0
-    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 10):
+    t_end = time.perf_counter() + CPU_BUDGET_S
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
         t0 = time.perf_counter()
-        oracle.timemix(case)
+        run(case)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {
-        "value": B * T * C / med,
-        "unit": "tokens*channels/s",
+        "value": elements / med,
+        "unit": "tokens\u00b7channels/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"full workload B{B} T{T} C{C}, oracle.timemix (fp64 C, OpenMP over channels: "
-                  f"token shift, numerator/denominator recurrence, final state), median of {len(times)} runs",
+        "sample": f"{sample}; fp64 C oracle with OpenMP over channels, median of {len(times)} runs",
     }
 
 
@@ -110,18 +126,139 @@ def copy_kernel(args):
     n = int(args.copy_mib * 2**20) // 4
     a = torch.empty(n, dtype=torch.float32, device="cuda:0").normal_()
     b = torch.empty_like(a)
-    for _ in range(args.warmup):
+    for _ in range(args.warmup or 2):
         b.copy_(a)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = args.steps or 10
     s.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         b.copy_(a)
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / args.steps
+    ms = s.elapsed_time(e) / steps
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms_per_copy": ms,
                       "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
+
+
+class Setup:
+    """Device buffers and the raw ctypes calls of one workload."""
+
+    def __init__(self, name, args, torch, rw, wi, np):
+        self.name = name
+        idx, self.desc = WORKLOADS[name]
+        wl = wi.WORKLOADS[idx]
+        self.B, self.T, self.C = wl.B, wl.T, wl.C
+        B, T, C = self.B, self.T, self.C
+        dev = torch.device("cuda:0")
+        vp = ctypes.c_void_p
+        stream = torch.cuda.current_stream(dev)
+        hs = vp(stream.cuda_stream)
+        self.stream = stream
+        tdt = {"f16": torch.float16, "f32": torch.float32}
+        esz = {"f16": 2, "f32": 4}
+        ei, eo = esz[wl.in_dtype], esz[wl.out_dtype]
+        self.io = f"{wl.in_dtype}->{wl.out_dtype}"
+
+        def dev_t(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        opts = rw.Opts()
+        opts.size = ctypes.sizeof(rw.Opts)
+        opts.in_dtype = rw.RWKV_F16 if wl.in_dtype == "f16" else rw.RWKV_F32
+        opts.out_dtype = rw.RWKV_F16 if wl.out_dtype == "f16" else rw.RWKV_F32
+        opts.chunk_len = args.chunk_len
+        opts.algo = {"auto": 0, "sequential": 1, "chunked": 2}[args.algo]
+        self.opts = opts
+        self.keep = []
+        case = wi.workload_inputs(idx)
+
+        if wl.kind == "step":
+            self.entry = "rwkv4_wkv_step"
+            self.fn = rw.lib.rwkv4_wkv_step
+            self.launches_per_step = len(case)
+            self.elements = len(case) * B * C
+            # per launch: k, v, r read and y written (2 B each), state read and written
+            # (12 B each), w and u (4 B per channel)
+            self.launch_bytes = 4 * 2 * B * C + 2 * 12 * B * C + 8 * C
+            calls = []
+            for layer in case:
+                t = {n: dev_t(layer[n]) for n in ("k", "v", "r", "w", "u", "state")}
+                y = torch.empty((B, C), dtype=tdt[wl.out_dtype], device=dev)
+                self.keep.append((t, y))
+                calls.append((B, C, vp(t["w"].data_ptr()), vp(t["u"].data_ptr()), vp(t["k"].data_ptr()),
+                              vp(t["v"].data_ptr()), vp(t["r"].data_ptr()), vp(y.data_ptr()),
+                              vp(t["state"].data_ptr()), opts.in_dtype, opts.out_dtype, hs))
+            self.sets = [calls]  # 40 layers of 42 MB each: no rotation needed beyond the layers
+            self.cpu_case = case[:4]
+            self.cpu_elements = 4 * B * C
+            self.cpu_sample = "4 of the 40 decode layers (B256 C5120, one token each)"
+            return
+
+        E = B * T * C
+        self.elements = E
+        self.launches_per_step = 1
+        if wl.kind == "timemix":
+            self.entry = "rwkv4_timemix_fused"
+            self.fn = rw.lib.rwkv4_timemix_fused
+            # x, k, v read and y written once, x_prev read and x_last written, mix_r/k/v, w, u
+            # (fp32 per channel; mix_k/v are read even when xk/xv are not requested), state out
+            self.launch_bytes = 3 * ei * E + eo * E + 2 * ei * B * C + 5 * 4 * C + 3 * 4 * B * C
+            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in ("x", "k", "v")}
+            sh = {n: dev_t(case[n]) for n in ("x_prev", "mix_k", "mix_v", "mix_r", "w", "u")}
+            self.keep.append(sh)
+            set_bytes = (3 * ei + eo) * E
+            R = max(2, math.ceil(args.rotate_gib * 2**30 / set_bytes))
+            self.sets = []
+            for _ in range(R):
+                s = dict(x=h["x"].to(dev), k=h["k"].to(dev), v=h["v"].to(dev),
+                         y=torch.empty((B, T, C), dtype=tdt[wl.out_dtype], device=dev),
+                         x_last=torch.empty((B, C), dtype=tdt[wl.in_dtype], device=dev),
+                         state_out=torch.empty((3, B, C), dtype=torch.float32, device=dev))
+                self.keep.append(s)
+                self.sets.append([(B, T, C, vp(s["x"].data_ptr()), vp(sh["x_prev"].data_ptr()),
+                                   vp(s["x_last"].data_ptr()), vp(sh["mix_k"].data_ptr()),
+                                   vp(sh["mix_v"].data_ptr()), vp(sh["mix_r"].data_ptr()),
+                                   vp(s["k"].data_ptr()), vp(s["v"].data_ptr()), vp(sh["w"].data_ptr()),
+                                   vp(sh["u"].data_ptr()), vp(s["y"].data_ptr()), None, None, None,
+                                   vp(s["state_out"].data_ptr()), hs, ctypes.byref(opts))])
+        else:
+            self.entry = "rwkv4_wkv_forward"
+            self.fn = rw.lib.rwkv4_wkv_forward
+            names = ["k", "v"] + (["r"] if wl.gated else [])
+            # k, v (and r) read, y written, w and u, the prior state read (if any), state out
+            self.launch_bytes = ((len(names) * ei + eo) * E + 8 * C + (12 * B * C if wl.prior else 0)
+                                 + 12 * B * C)
+            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in names}
+            sh = {n: dev_t(case[n]) for n in ("w", "u")}
+            if wl.prior:
+                sh["state_in"] = dev_t(case["state_in"])
+            self.keep.append(sh)
+            set_bytes = (len(names) * ei + eo) * E
+            R = max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
+            self.sets = []
+            for _ in range(R):
+                s = {n: h[n].to(dev) for n in names}
+                s["y"] = torch.empty((B, T, C), dtype=tdt[wl.out_dtype], device=dev)
+                s["state_out"] = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+                o = rw.Opts()
+                ctypes.memmove(ctypes.byref(o), ctypes.byref(opts), ctypes.sizeof(o))
+                o.r = s["r"].data_ptr() if wl.gated else None
+                s["opts"] = o
+                self.keep.append(s)
+                self.sets.append([(B, T, C, vp(sh["w"].data_ptr()), vp(sh["u"].data_ptr()),
+                                   vp(s["k"].data_ptr()), vp(s["v"].data_ptr()), vp(s["y"].data_ptr()),
+                                   vp(sh["state_in"].data_ptr()) if wl.prior else None,
+                                   vp(s["state_out"].data_ptr()), hs, ctypes.byref(o))])
+        self.cpu_case = case
+        self.cpu_elements = E
+        self.cpu_sample = f"the full workload B{B} T{T} C{C}"
+
+    def step(self, i, rw):
+        for call in self.sets[i % len(self.sets)]:
+            st = self.fn(*call)
+            if st != 0:
+                raise rw.RwkvError(st, rw.rwkv_last_error())
 
 
 def main():
@@ -136,104 +273,60 @@ def main():
     import rwkv_wkv_linear_amd as rw
     import wkv_inputs as wi
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = wi.WORKLOADS[2]
-    B, T, C = wl.B, wl.T, wl.C
-    case = wi.workload_inputs(2)
-    E = B * T * C
+    torch.cuda.set_device(torch.device("cuda:0"))
+    name = args.workload
+    su = Setup(name, args, torch, rw, wi, np)
+    default_steps = {"timemix14b": 1000, "plain169m": 1000, "gated169m": 500, "decode14b": 100, "long": 50}
+    K = args.steps if args.steps is not None else default_steps[name]
+    W = args.warmup if args.warmup is not None else max(5, K // 20)
 
-    # resident inputs, R rotated sets of (x, k, v, y, x_last, state_out)
-    h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in ("x", "k", "v")}
-    shared = {n: torch.from_numpy(np.ascontiguousarray(case[n])).to(dev)
-              for n in ("x_prev", "mix_k", "mix_v", "mix_r", "w", "u")}
-    set_bytes = 4 * E * 2 + B * C * 2 + 3 * B * C * 4
-    R = max(2, math.ceil(args.rotate_gib * 2**30 / set_bytes))
-    sets = []
-    for _ in range(R):
-        sets.append(dict(x=h["x"].to(dev), k=h["k"].to(dev), v=h["v"].to(dev),
-                         y=torch.empty((B, T, C), dtype=torch.float16, device=dev),
-                         x_last=torch.empty((B, C), dtype=torch.float16, device=dev),
-                         state_out=torch.empty((3, B, C), dtype=torch.float32, device=dev)))
-    stream = torch.cuda.current_stream(dev)
-    opts = rw.Opts()
-    opts.size = ctypes.sizeof(rw.Opts)
-    opts.in_dtype = rw.RWKV_F16
-    opts.out_dtype = rw.RWKV_F16
-    opts.chunk_len = args.chunk_len
-    opts.algo = {"auto": 0, "sequential": 1, "chunked": 2}[args.algo]
-    vp = ctypes.c_void_p
-    hs = vp(stream.cuda_stream)
-    fn = rw.lib.rwkv4_timemix_fused
-    calls = []
-    for s in sets:
-        calls.append((B, T, C, vp(s["x"].data_ptr()), vp(shared["x_prev"].data_ptr()), vp(s["x_last"].data_ptr()),
-                      vp(shared["mix_k"].data_ptr()), vp(shared["mix_v"].data_ptr()), vp(shared["mix_r"].data_ptr()),
-                      vp(s["k"].data_ptr()), vp(s["v"].data_ptr()), vp(shared["w"].data_ptr()),
-                      vp(shared["u"].data_ptr()), vp(s["y"].data_ptr()), None, None, None,
-                      vp(s["state_out"].data_ptr()), hs, ctypes.byref(opts)))
-
-    def step(i):
-        st = fn(*calls[i % R])
-        if st != 0:
-            raise rw.RwkvError(st, rw.rwkv_last_error())
-
-    for i in range(args.warmup):
-        step(i)
+    for i in range(W):
+        su.step(i, rw)
     torch.cuda.synchronize()
 
-    # The timed region: K back-to-back launches on `stream`, bracketed by one pair of HIP
-    # events on that stream and by device synchronisations.  A timing event between
+    # The timed region: K steps launched back to back on the stream, bracketed by one pair
+    # of HIP events on that stream and by device synchronisations.  A timing event between
     # launches is a marker packet with its own cache maintenance that slows the launch it
     # brackets, so per-launch events would not measure the launches as they run in a layer
     # loop; the pair gives their average duration.
-    K = args.steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    ev0.record(su.stream)
     for i in range(K):
-        step(args.warmup + i)
-    ev1.record(stream)
+        su.step(W + i, rw)
+    ev1.record(su.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_avg_ms = ev0.elapsed_time(ev1) / K
+    launch_avg_ms = ev0.elapsed_time(ev1) / (K * su.launches_per_step)
 
-    # algorithmic bytes per launch: x, k, v read and y written once (2 B each per element),
-    # plus x_prev, x_last (fp16 rows), mix_r/mix_k/mix_v, w, u (fp32 per channel; mix_k/v are
-    # read by the kernel even when xk/xv are not requested) and the fp32 state written
-    algo_bytes = 8 * E + 2 * 2 * B * C + 5 * 4 * C + 3 * 4 * B * C
-    achieved = algo_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = counters_traffic()
-    chunk = args.chunk_len
-    if args.algo != "sequential" and chunk == 0:
-        chunk = None
+    achieved = su.launch_bytes / (launch_avg_ms * 1e-3) / 1e9
+    traffic = counters_traffic() if name == "timemix14b" else None
+    chunk = args.chunk_len if args.chunk_len else None
     result = {
-        "metric": "WKV tokens*channels/s (and achieved HBM GB/s of the WKV kernel vs MI355X peak), "
-                  "RWKV-4 14B layer shape",
-        "value": E * K / wall,
-        "unit": "tokens*channels/s",
+        "metric": "WKV tokens\u00b7channels/sec and achieved HBM GB/s (% of MI355X peak), "
+                  + ("14B shape" if name == "timemix14b" else su.desc),
+        "value": su.elements * K / wall,
+        "unit": "tokens\u00b7channels/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": W,
         "ms_per_step": wall * 1e3 / K,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "B": B, "T": T, "C": C, "io_dtype": "f16",
-                   "entry_point": "rwkv4_timemix_fused", "algo": args.algo, "chunk_len": chunk,
-                   "rotated_sets": R},
+        "config": {"workload": su.desc, "B": su.B, "T": su.T, "C": su.C, "io_dtype": su.io,
+                   "entry_point": su.entry, "launches_per_step": su.launches_per_step,
+                   "algo": args.algo, "chunk_len": chunk, "rotated_sets": len(su.sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
-        "kernel_avg_us": kern_avg_ms * 1e3,
-        "algorithmic_bytes_per_launch": algo_bytes,
+        "kernel_avg_us": launch_avg_ms * 1e3,
+        "algorithmic_bytes_per_launch": su.launch_bytes,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, B, T, C)
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = None if args.no_cpu_baseline else \
+        cpu_baseline(name, su.cpu_case, su.cpu_elements, su.cpu_sample)
     print(json.dumps(result), flush=True)
 
 

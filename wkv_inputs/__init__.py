@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for the RWKV-4 WKV time-mixing path.
 
-This module is shared by the tests, the benchmark and the checker, and it holds
+This module is shared by the tests, the benchmark and the oracle's tests, and it holds
 none of the recurrence's arithmetic: it only draws random arrays, rounds them
 to the I/O dtype, and evaluates the per-channel initialisation recipe for the
 decay and bonus parameters.
