@@ -172,6 +172,8 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         if (p && !aligned(p, 16)) vec16 = false;
     a.vec16 = vec16 ? 1 : 0;
     a.vec16y = (a.y && aligned(a.y, 16) && (C % (int64_t)(16 / eo)) == 0) ? 1 : 0;
+    a.vecs = ((C % 4) == 0 && (!a.state_in || aligned(a.state_in, 16)) &&
+              (!a.state_out || aligned(a.state_out, 16))) ? 1 : 0;
 
     hipError_t e;
     if (T == 0) {

@@ -180,12 +180,22 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
     load_param4(a.w, c0, nch, w);
     load_param4(a.u, c0, nch, u);
     St s[4];
+    const bool vs = a.vecs != 0 && nch == 4;  // the lane's state is three aligned float4
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        w[q] = finite_decay(w[q]);
-        s[q] = st_empty();
-        if (a.state_in && q < nch)
-            s[q] = st_load(a.state_in[sc + q], a.state_in[BC + sc + q], a.state_in[2 * BC + sc + q]);
+    for (int q = 0; q < 4; ++q) w[q] = finite_decay(w[q]);
+    if (a.state_in && vs) {
+        const f4 A = *reinterpret_cast<const f4 *>(a.state_in + sc);
+        const f4 Bq = *reinterpret_cast<const f4 *>(a.state_in + BC + sc);
+        const f4 P = *reinterpret_cast<const f4 *>(a.state_in + 2 * BC + sc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] = st_load(A[q], Bq[q], P[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s[q] = st_empty();
+            if (a.state_in && q < nch)
+                s[q] = st_load(a.state_in[sc + q], a.state_in[BC + sc + q], a.state_in[2 * BC + sc + q]);
+        }
     }
     float mk[4], mv[4], mr[4], xs[4];
     if constexpr (MODE == MODE_TIMEMIX) {
@@ -232,7 +242,18 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
             if (a.xv_out) store4(static_cast<TIn *>(a.xv_out), off, nch, vec, xvo);
         }
     }
-    if (a.state_out) {
+    if (a.state_out && vs) {
+        f4 A, Bq, P;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            A[q] = s[q].a;
+            Bq[q] = s[q].b;
+            P[q] = st_logmax(s[q], w[q]);
+        }
+        *reinterpret_cast<f4 *>(a.state_out + sc) = A;
+        *reinterpret_cast<f4 *>(a.state_out + BC + sc) = Bq;
+        *reinterpret_cast<f4 *>(a.state_out + 2 * BC + sc) = P;
+    } else if (a.state_out) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (q < nch) {
