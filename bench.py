@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="timemix14b", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
-    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "sequential"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "two_pass", "sequential"])
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-kernel", action="store_true",
@@ -168,7 +168,7 @@ class Setup:
         opts.in_dtype = rw.RWKV_F16 if wl.in_dtype == "f16" else rw.RWKV_F32
         opts.out_dtype = rw.RWKV_F16 if wl.out_dtype == "f16" else rw.RWKV_F32
         opts.chunk_len = args.chunk_len
-        opts.algo = {"auto": 0, "sequential": 1, "chunked": 2}[args.algo]
+        opts.algo = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3}[args.algo]
         self.opts = opts
         self.keep = []
         case = wi.workload_inputs(idx)

@@ -71,9 +71,15 @@ typedef enum rwkv_status {
 typedef enum rwkv_dtype { RWKV_F32 = 0, RWKV_F16 = 1 } rwkv_dtype;
 
 typedef enum rwkv_algo {
-    RWKV_ALGO_AUTO = 0,        /* pick by shape */
+    RWKV_ALGO_AUTO = 0,        /* pick by shape: sequential for large B*C (or T <= 1), else
+                                  chunked */
     RWKV_ALGO_SEQUENTIAL = 1,  /* one lane per (b, 4 channels), loop over T (large B*C) */
-    RWKV_ALGO_CHUNKED = 2      /* chunked scan over T with a cross-workgroup look-back */
+    RWKV_ALGO_CHUNKED = 2,     /* chunked scan over T in one launch: each tile gets its
+                                  incoming state from its predecessors through a
+                                  cross-workgroup look-back (long sequences) */
+    RWKV_ALGO_TWO_PASS = 3     /* chunked scan in two launches: the aggregates of the tiles,
+                                  then every tile folds its predecessors' aggregates (no waiting
+                                  between workgroups; capturable; costs one more read of k, v) */
 } rwkv_algo;
 
 /*
@@ -93,7 +99,8 @@ typedef struct rwkv4_opts {
     void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
                                 else device memory of workspace_bytes >= the size
                                 rwkv4_workspace_bytes() reports, zero-filled by the
-                                caller once before its first use, then reusable */
+                                caller once before its first use (RWKV_ALGO_CHUNKED
+                                relies on it), then reusable */
     size_t workspace_bytes;
 } rwkv4_opts;
 
@@ -106,9 +113,11 @@ typedef struct rwkv4_opts {
  *   state_in     [3,B,C] fp32 prior state, or NULL for the empty state.
  *   state_out    [3,B,C] fp32 state after the T tokens, or NULL.  May equal
  *                state_in exactly (in-place update); no other overlap is allowed.
- * Concurrent calls on different streams that use the chunked scan must not share
- * a workspace (pass opts->workspace).  The chunked scan is not capturable into a
- * HIP graph (its workspace is stamped per launch from the host).
+ * Concurrent calls on different streams that use a chunked scan must not share
+ * a workspace (pass opts->workspace).  The single-launch chunked scan
+ * (RWKV_ALGO_CHUNKED) is not capturable into a HIP graph: its workspace is stamped per
+ * launch from the host.  The sequential and two-pass algorithms are, given an explicit
+ * opts->workspace (the library-cached one is allocated on first use).
  */
 rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C,
                               const float *w, const float *u,

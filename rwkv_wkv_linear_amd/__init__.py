@@ -20,8 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "rwkvwkv.h")
 
 RWKV_OK, RWKV_ERR_ARG, RWKV_ERR_DTYPE, RWKV_ERR_ALIGN, RWKV_ERR_HIP, RWKV_ERR_NOMEM = 0, -1, -2, -3, -4, -5
 RWKV_F32, RWKV_F16 = 0, 1
-RWKV_ALGO_AUTO, RWKV_ALGO_SEQUENTIAL, RWKV_ALGO_CHUNKED = 0, 1, 2
-_ALGOS = {"auto": 0, "sequential": 1, "chunked": 2, 0: 0, 1: 1, 2: 2}
+RWKV_ALGO_AUTO, RWKV_ALGO_SEQUENTIAL, RWKV_ALGO_CHUNKED, RWKV_ALGO_TWO_PASS = 0, 1, 2, 3
+_ALGOS = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3, 0: 0, 1: 1, 2: 2, 3: 3}
 
 
 class Opts(ctypes.Structure):

@@ -112,7 +112,7 @@ rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
     rwkv_status s;
     if ((s = check_dtype(o->in_dtype, "opts->in_dtype")) != RWKV_OK) return s;
     if ((s = check_dtype(o->out_dtype, "opts->out_dtype")) != RWKV_OK) return s;
-    if (o->algo < RWKV_ALGO_AUTO || o->algo > RWKV_ALGO_CHUNKED)
+    if (o->algo < RWKV_ALGO_AUTO || o->algo > RWKV_ALGO_TWO_PASS)
         return fail(RWKV_ERR_ARG, "opts->algo %d is not a rwkv_algo", (int)o->algo);
     if (o->chunk_len != 0) {
         const int c = o->chunk_len;
@@ -195,8 +195,10 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
                         chunk, cmax);
         chunk = cmax;
     }
+    const int64_t nTT = (T + chunk - 1) / chunk;
+    const bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
     ChunkWorkspace ws{};
-    if (T > chunk) {  // more than one tile per chain: the look-back needs scratch
+    if (T > chunk) {  // more than one tile per chain: the prefixes need scratch
         const size_t need = chunk_workspace_bytes(B, T, C, chunk);
         void *base = o.workspace;
         if (base) {
@@ -208,10 +210,10 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
             if (s != RWKV_OK) return s;
         }
         chunk_workspace_carve(base, B, T, C, chunk, &ws);
-        ws.epoch = next_epoch();
+        if (!two_pass) ws.epoch = next_epoch();
     }
-    e = launch_chunked(a, chunk, ws, stream);
-    if (e != hipSuccess) return hip_fail(e, "launch (chunked)");
+    e = two_pass ? launch_chunked_2pass(a, chunk, ws, stream) : launch_chunked(a, chunk, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, two_pass ? "launch (two-pass chunked)" : "launch (chunked)");
     return ok();
 }
 

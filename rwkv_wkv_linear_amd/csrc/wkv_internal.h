@@ -37,7 +37,8 @@ struct ForwardArgs {
 // Chunked-scan scratch: per tile and channel four 64-bit words (a, b, key, age), each the
 // fp32 value tagged with (epoch << 2 | kind) in its high half.
 struct ChunkWorkspace {
-    uint64_t *words;  // [tiles][4][64]
+    uint64_t *words;  // single pass: [tiles][4][64] tagged words
+    float *aggs;      // two passes: [tiles][64][4] tile aggregates
     uint32_t *err;    // one word: set when a look-back wait gave up
     uint32_t epoch;   // per-launch stamp; words of other launches never match
 };
@@ -59,6 +60,14 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
 hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s);
 hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
                           hipStream_t s);
+// Two launches: tile aggregates, then every tile folds its predecessors' aggregates.
+hipError_t launch_chunked_2pass(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
+                                hipStream_t s);
+// Longest chain (time tiles per (b, channel tile)) the two-pass scan takes by default: none.
+// Measured on the 14B layer shape, the aggregate pass (8.1 us) plus the emit pass (13.8 us)
+// cost more than the single pass's look-back wait (18.7 us in all), so AUTO keeps the single
+// pass; RWKV_ALGO_TWO_PASS stays available (graph-capturable, no cross-workgroup waiting).
+constexpr int kTwoPassMaxTiles = 0;
 // T == 0: state_out <- state_in (or the empty state), x_last <- x_prev (or zeros).
 hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s);
 

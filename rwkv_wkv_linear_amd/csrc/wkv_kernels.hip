@@ -361,9 +361,116 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 //   incoming state scale p - kmax <= 60, so it cannot overflow.
 // A lane outside the guard runs the exact per-token max-trick instead (same results within
 // rounding; the tests drive both paths).
+// How a tile gets its incoming state: from its predecessors in the same launch (single
+// pass, decoupled look-back) or from tile aggregates a previous launch wrote (two passes).
+constexpr int PREFIX_LOOKBACK = 0, PREFIX_AGGS = 1;
+
 constexpr float kGuardSpread = 40.f;
 constexpr float kGuardBonus = -20.f;
 constexpr float kGuardState = 60.f;
+
+// Phase A of a tile: wave wv stages its L rows (tokens t0 .. t0+L-1 of the tile) of each
+// of the NT tensors in src into LDS rows[NT][TW][64].  With 16-byte vectors (vec16) each
+// global_load_lds_dwordx4 moves RPI whole 128-B (fp16) or 256-B (fp32) rows, and no VGPR holds
+// a load in flight; otherwise each lane loads its own channel in rolled batches of 4 rows (a
+// rare path, kept from setting the kernel's register footprint).  Rows past T and chunks past
+// C read a valid clamped address whose data is never used.
+template <typename TIn, int NT, int L>
+__device__ __forceinline__ void stage_rows(const TIn *const *src, TIn *rows, int TW, int wv, int lane, int64_t b,
+                                           int64_t T, int64_t C, int64_t ct, int64_t tile_t0, int64_t t0,
+                                           int64_t cs, bool vec16) {
+    constexpr int CW = kTileChannels;
+    if (vec16) {
+        constexpr int CH16 = 16 / (int)sizeof(TIn);  // channels per 16-byte chunk
+        constexpr int CHUNKS = CW / CH16;           // chunks per row: 8 (fp16) or 16 (fp32)
+        constexpr int RPI = 64 / CHUNKS;            // rows per instruction: 8 or 4
+        const int q = lane % CHUNKS, rsub = lane / CHUNKS;
+        int64_t cq = ct * CW + q * CH16;
+        if (cq >= C) cq = 0;
+#pragma unroll
+        for (int tsr = 0; tsr < NT; ++tsr) {
+#pragma unroll
+            for (int j = 0; j < L / RPI; ++j) {
+                const int r = wv * L + j * RPI;
+                const int64_t t = std::min<int64_t>(tile_t0 + r + rsub, T - 1);
+                dma16(src[tsr] + (b * T + t) * C + cq, rows + ((size_t)tsr * TW + r) * CW);
+            }
+        }
+    } else {
+        const int64_t tl = std::min<int64_t>(t0, T - 1);
+        const int last = (int)std::min<int64_t>(L - 1, T - 1 - tl);
+#pragma unroll
+        for (int tsr = 0; tsr < NT; ++tsr) {
+            const TIn *col = src[tsr] + (b * T + tl) * C + cs;
+#pragma unroll 1
+            for (int i0 = 0; i0 < L; i0 += 4) {
+                TIn tmp[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tmp[i] = col[(int64_t)std::min(i0 + i, last) * C];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rows[((size_t)tsr * TW + wv * L + i0 + i) * CW + lane] = tmp[i];
+            }
+        }
+    }
+}
+
+// Phase B of a tile: the summary of one wave's nval tokens from the empty state (kr, vr point
+// at the lane's first staged key and value).  Padded tokens (i >= nval) get weight X = 0 and
+// decay 1, so they leave every recurrence unchanged.  Sets kmax (the largest key) and fast
+// (whether the linear-space guard holds; else the exact per-token max-trick ran).
+template <typename TIn, int L>
+__device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nval, float wc, float uc, float ew,
+                                           float &kmax, bool &fast) {
+    constexpr int CW = kTileChannels;
+    kmax = -INFINITY;
+    float kmin = INFINITY;
+    St sum = st_empty();
+    float xk[L], vb[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        xk[i] = (float)kr[i * CW];
+        vb[i] = (float)vr[i * CW];
+    }
+    if (nval == L) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            kmax = fmaxf(kmax, xk[i]);
+            kmin = fminf(kmin, xk[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            kmax = fmaxf(kmax, i < nval ? xk[i] : -INFINITY);
+            kmin = fminf(kmin, i < nval ? xk[i] : INFINITY);
+        }
+    }
+    fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
+    if (fast) {
+        float nn = 0.f, dd = 0.f;
+        if (nval == L) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const float X = ex(xk[i] - kmax);
+                nn = fmaf(ew, nn, X * vb[i]);
+                dd = fmaf(ew, dd, X);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const float X = (i < nval) ? ex(xk[i] - kmax) : 0.f;
+                const float e = (i < nval) ? ew : 1.f;
+                nn = fmaf(e, nn, X * vb[i]);
+                dd = fmaf(e, dd, X);
+            }
+        }
+        sum = St{nn, dd, kmax, 0.f};
+    } else {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            if (i < nval) absorb(sum, wc, xk[i], vb[i]);
+    }
+    return sum;
+}
 
 // Linear-space emit of one wave's L tokens when all of them are valid: y_i from the running
 // numerator/denominator (nn, dd, scaled by e^{-kmax}), then the recurrence step.  With
@@ -437,7 +544,7 @@ __device__ __forceinline__ void emit_full(const TIn *kr, const TIn *vr, const TI
 // whose data is never used.  The weights X_i are recomputed from the staged keys in
 // phase E rather than held in VGPRs across the look-back, which keeps the register
 // footprint low enough for every workgroup of a layer-sized call to be resident at once.
-template <typename TIn, typename TOut, int MODE, int L>
+template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
 __global__ void __launch_bounds__(1024)
     wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
     constexpr int CW = kTileChannels;
@@ -469,43 +576,47 @@ __global__ void __launch_bounds__(1024)
     const TIn *V = static_cast<const TIn *>(a.v);
     const TIn *GR = static_cast<const TIn *>(MODE == MODE_GATED ? a.r : a.x);
 
+    const int64_t chain = (b * nCT + ct) * nTT;
+
+    // Two passes: the aggregates of tiles 0 .. tt-1 are complete before this launch.  Wave wv
+    // loads its share (issued before the row loads, so it lands first) and folds it, wave 0
+    // starting from state_in; the shares are combined in order through LDS while the rows are
+    // still in flight.  The result is state_in + AGG(0) + ... + AGG(tt-1), folded in a fixed
+    // order.
+    St prefix = st_empty();
+    St part = st_empty();
+    int q = 0;
+    if constexpr (PREFIX == PREFIX_AGGS) {
+        if (tt > 0) {
+            q = (int)((tt + S - 1) / S);
+            const int lo = wv * q, hi = std::min<int>(lo + q, (int)tt);
+            const f4 *src = reinterpret_cast<const f4 *>(ws.aggs) + (chain + lo) * CW + lane;
+            bool have = false;
+            if (wv == 0 && a.state_in && cok) {
+                part = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
+                have = true;
+            }
+            const float w_pre = finite_decay(a.w[cs]);
+            for (int j0 = lo; j0 < hi; j0 += 4) {
+                f4 x[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (j0 + m < hi) x[m] = src[(j0 - lo + m) * CW];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (j0 + m < hi) {
+                        const St g = St{x[m][0], x[m][1], x[m][2], x[m][3]};
+                        part = have ? combine(part, g, (float)TW, w_pre) : g;
+                        have = true;
+                    }
+            }
+        }
+    }
+
     // Phase A: stage this wave's rows.
     {
         const TIn *src[3] = {K, V, GR};
-        if (a.vec16) {
-            constexpr int CH16 = 16 / (int)sizeof(TIn);  // channels per 16-byte chunk
-            constexpr int CHUNKS = CW / CH16;           // chunks per row: 8 (fp16) or 16 (fp32)
-            constexpr int RPI = 64 / CHUNKS;            // rows per instruction: 8 or 4
-            const int q = lane % CHUNKS, rsub = lane / CHUNKS;
-            int64_t cq = ct * CW + q * CH16;
-            if (cq >= C) cq = 0;
-#pragma unroll
-            for (int tsr = 0; tsr < NT; ++tsr) {
-#pragma unroll
-                for (int j = 0; j < L / RPI; ++j) {
-                    const int r = wv * L + j * RPI;
-                    const int64_t t = std::min<int64_t>(tile_t0 + r + rsub, a.T - 1);
-                    dma16(src[tsr] + (b * a.T + t) * C + cq, rows + ((size_t)tsr * TW + r) * CW);
-                }
-            }
-        } else {
-            // rolled batches of 4 rows keep this (rare) path's register footprint from
-            // setting the kernel's
-            const int64_t tl = std::min<int64_t>(t0, a.T - 1);
-            const int last = (int)std::min<int64_t>(L - 1, a.T - 1 - tl);
-#pragma unroll
-            for (int tsr = 0; tsr < NT; ++tsr) {
-                const TIn *col = src[tsr] + (b * a.T + tl) * C + cs;
-#pragma unroll 1
-                for (int i0 = 0; i0 < L; i0 += 4) {
-                    TIn tmp[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) tmp[i] = col[(int64_t)std::min(i0 + i, last) * C];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rows[((size_t)tsr * TW + wv * L + i0 + i) * CW + lane] = tmp[i];
-                }
-            }
-        }
+        stage_rows<TIn, NT, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
     }
     // per-channel parameters (and the time-mix token before wave 0's first) load meanwhile
     const float w_raw = a.w[cs], u_raw = a.u[cs];
@@ -525,6 +636,26 @@ __global__ void __launch_bounds__(1024)
         mv = cok ? mv_raw : 0.f;
     }
     const float ew = ex(wc), eu = ex(uc);
+    if (tt == 0) {
+        if (a.state_in && cok)
+            prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
+    } else if constexpr (PREFIX == PREFIX_AGGS) {
+        sF[(0 * S + wv) * CW + lane] = part.a;
+        sF[(1 * S + wv) * CW + lane] = part.b;
+        sF[(2 * S + wv) * CW + lane] = part.k;
+        sF[(3 * S + wv) * CW + lane] = part.n;
+        __syncthreads();
+        for (int j = 0; j < S; ++j) {
+            const int lj = j * q;
+            if (lj < (int)tt) {
+                const St pj = St{sF[(0 * S + j) * CW + lane], sF[(1 * S + j) * CW + lane],
+                                 sF[(2 * S + j) * CW + lane], sF[(3 * S + j) * CW + lane]};
+                const float span = (float)((std::min(lj + q, (int)tt) - lj) * TW);
+                prefix = (j == 0) ? pj : combine(prefix, pj, span, wc);
+            }
+        }
+        __syncthreads();  // the wave summaries reuse sF next
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
     __builtin_amdgcn_wave_barrier();
 
@@ -532,57 +663,10 @@ __global__ void __launch_bounds__(1024)
     const TIn *vr = rows + ((size_t)1 * TW + wv * L) * CW + lane;
     const TIn *gr = rows + ((size_t)2 * TW + wv * L) * CW + lane;
 
-    // Phase B: summary of the wave's tokens from the empty state.  Padded tokens
-    // (i >= nval) get weight X = 0 and decay 1, so they leave every recurrence unchanged.
-    float kmax = -INFINITY, kmin = INFINITY;
-    St sum = st_empty();
+    // Phase B: summary of the wave's tokens from the empty state.
+    float kmax;
     bool fast;
-    {
-        float xk[L], vb[L];
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-            xk[i] = (float)kr[i * CW];
-            vb[i] = (float)vr[i * CW];
-        }
-        if (nval == L) {
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-                kmax = fmaxf(kmax, xk[i]);
-                kmin = fminf(kmin, xk[i]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-                kmax = fmaxf(kmax, i < nval ? xk[i] : -INFINITY);
-                kmin = fminf(kmin, i < nval ? xk[i] : INFINITY);
-            }
-        }
-        fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
-        if (fast) {
-            float nn = 0.f, dd = 0.f;
-            if (nval == L) {
-#pragma unroll
-                for (int i = 0; i < L; ++i) {
-                    const float X = ex(xk[i] - kmax);
-                    nn = fmaf(ew, nn, X * vb[i]);
-                    dd = fmaf(ew, dd, X);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < L; ++i) {
-                    const float X = (i < nval) ? ex(xk[i] - kmax) : 0.f;
-                    const float e = (i < nval) ? ew : 1.f;
-                    nn = fmaf(e, nn, X * vb[i]);
-                    dd = fmaf(e, dd, X);
-                }
-            }
-            sum = St{nn, dd, kmax, 0.f};
-        } else {
-#pragma unroll
-            for (int i = 0; i < L; ++i)
-                if (i < nval) absorb(sum, wc, xk[i], vb[i]);
-        }
-    }
+    const St sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast);
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
@@ -598,12 +682,13 @@ __global__ void __launch_bounds__(1024)
         const int lj = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - (tile_t0 + (int64_t)j * L)));
         excl = combine(excl, sj, (float)lj, wc);
     }
-    const int64_t chain = (b * nCT + ct) * nTT;
     const bool anchor = (tt % M) == 0, last = tt == nTT - 1;
     St agg = st_empty();
-    if (wv == S - 1) {
-        agg = combine(excl, sum, (float)wlen, wc);
-        if (nTT > 1 && !anchor && !last) publish(ws, chain + tt, kAgg, agg, lane);
+    if constexpr (PREFIX == PREFIX_LOOKBACK) {
+        if (wv == S - 1) {
+            agg = combine(excl, sum, (float)wlen, wc);
+            if (nTT > 1 && !anchor && !last) publish(ws, chain + tt, kAgg, agg, lane);
+        }
     }
 
     // Phase D: the tile's incoming state.  Anchor tiles (every M-th, tile 0 included) publish
@@ -611,16 +696,11 @@ __global__ void __launch_bounds__(1024)
     // the prefix is INCL(a) + AGG(a+1) + ... + AGG(tt-1), folded in that fixed order whatever
     // the timing, so results are bitwise reproducible.  The waves share the polling: wave w
     // folds a contiguous part, then every wave folds the parts in order.
-    St prefix = st_empty();
-    if (tt == 0) {
-        if (a.state_in && cok)
-            prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
-    } else {
+    if (PREFIX == PREFIX_LOOKBACK && tt > 0) {
         const int a0 = (int)(((tt - 1) / M) * M);
         const int cnt = (int)tt - a0;
-        const int q = (cnt + S - 1) / S;
+        q = (cnt + S - 1) / S;
         const int lo = a0 + wv * q, hi = std::min(lo + q, (int)tt);
-        St part = st_empty();
         if (lo < hi) part = fold_published<kMaxAnchorGap / 4>(ws, chain, lo, hi, lo == a0, wc, (float)TW, lane);
         __syncthreads();  // sI reuses sF: every wave has folded its summaries (phase C)
         sI[(0 * S + wv) * CW + lane] = part.a;
@@ -638,7 +718,7 @@ __global__ void __launch_bounds__(1024)
             }
         }
     }
-    if (wv == S - 1 && nTT > 1 && anchor && !last)
+    if (PREFIX == PREFIX_LOOKBACK && wv == S - 1 && nTT > 1 && anchor && !last)
         publish(ws, chain + tt, kIncl, combine(prefix, agg, (float)tile_len, wc), lane);
     const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
 
@@ -767,6 +847,61 @@ __global__ void __launch_bounds__(1024)
 
 // ------------------------------------------------------------------------------------------
 
+// First pass of the two-pass scan: the aggregate (summary from the empty state) of every
+// time tile but the last of each chain, written as one float4 (a, b, key, age) per (tile,
+// channel) to ws.aggs.  Same tiling and phases A-B as wkv_tile_kernel, on k and v only.
+template <typename TIn, int L>
+__global__ void __launch_bounds__(1024)
+    wkv_tile_agg_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW) {
+    constexpr int CW = kTileChannels;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    TIn *rows = reinterpret_cast<TIn *>(smem);                                  // [2][TW][CW]
+    float *sF = reinterpret_cast<float *>(smem + (size_t)2 * TW * CW * sizeof(TIn));  // [4][S][CW]
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t BCT = a.B * nCT;
+    const int64_t tt = blockIdx.x / BCT;  // < nTT - 1: every tile here is full
+    const int64_t rem = blockIdx.x - tt * BCT;
+    const int64_t b = rem / nCT, ct = rem - b * nCT;
+    const int64_t c = ct * CW + lane;
+    const bool cok = c < a.C;
+    const int64_t tile_t0 = tt * TW, t0 = tile_t0 + (int64_t)wv * L;
+    const int64_t cs = cok ? c : 0;
+    {
+        const TIn *src[2] = {static_cast<const TIn *>(a.k), static_cast<const TIn *>(a.v)};
+        stage_rows<TIn, 2, L>(src, rows, TW, wv, lane, b, a.T, a.C, ct, tile_t0, t0, cs, a.vec16 != 0);
+    }
+    const float w_raw = a.w[cs], u_raw = a.u[cs];
+    const float wc = cok ? finite_decay(w_raw) : 0.f;
+    const float uc = cok ? u_raw : 0.f;
+    const float ew = ex(wc);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    float kmax;
+    bool fast;
+    const St sum = wave_summary<TIn, L>(rows + (size_t)wv * L * CW + lane, rows + ((size_t)TW + wv * L) * CW + lane,
+                                        cok ? L : 0, wc, uc, ew, kmax, fast);
+    sF[(0 * S + wv) * CW + lane] = sum.a;
+    sF[(1 * S + wv) * CW + lane] = sum.b;
+    sF[(2 * S + wv) * CW + lane] = sum.k;
+    sF[(3 * S + wv) * CW + lane] = sum.n;
+    __syncthreads();
+    if (wv == 0) {
+        St agg = st_empty();
+        for (int j = 0; j < S; ++j) {
+            const St sj = St{sF[(0 * S + j) * CW + lane], sF[(1 * S + j) * CW + lane],
+                             sF[(2 * S + j) * CW + lane], sF[(3 * S + j) * CW + lane]};
+            agg = (j == 0) ? sj : combine(agg, sj, (float)L, wc);
+        }
+        const int64_t chain = (b * nCT + ct) * nTT;
+        f4 out;
+        out[0] = agg.a;
+        out[1] = agg.b;
+        out[2] = agg.k;
+        out[3] = agg.n;
+        reinterpret_cast<f4 *>(ws.aggs)[(chain + tt) * CW + lane] = out;
+    }
+}
+
 template <typename TIn>
 __global__ void __launch_bounds__(256) wkv_passthrough_kernel(ForwardArgs a) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -799,7 +934,7 @@ hipError_t launch_seq_t(const ForwardArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int MODE, int L>
+template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
 hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
     const int S = chunk_len / L;
     const int nCT = (int)((a.C + kTileChannels - 1) / kTileChannels);
@@ -815,14 +950,29 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     // an anchor every 16 tiles: a chain of up to 16 tiles has no serial anchor hop at all
     const int M = kMaxAnchorGap;
     if (S < 4) return hipErrorInvalidConfiguration;  // each wave polls at most 16 / S tiles
-    hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, L>), dim3((unsigned)blocks), dim3(64 * S), lds, s, a,
-                       ws, S, nCT, nTT, chunk_len, M);
+    if (PREFIX == PREFIX_AGGS && nTT > 1) {
+        // first pass: aggregates of the first nTT - 1 time tiles (k and v rows only)
+        const int64_t agg_blocks = a.B * (int64_t)nCT * (nTT - 1);
+        const size_t lds1 = (size_t)2 * chunk_len * kTileChannels * sizeof(TIn) +
+                            (size_t)4 * S * kTileChannels * sizeof(float);
+        hipLaunchKernelGGL((wkv_tile_agg_kernel<TIn, L>), dim3((unsigned)agg_blocks), dim3(64 * S), lds1, s, a, ws,
+                           S, nCT, nTT, chunk_len);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, L, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
+                       a, ws, S, nCT, nTT, chunk_len, M);
     return hipGetLastError();
 }
 
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
-    return launch_tile<TIn, TOut, MODE, 16>(a, chunk_len, ws, s);
+    return launch_tile<TIn, TOut, MODE, 16, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
+}
+
+template <typename TIn, typename TOut, int MODE>
+hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
 }
 
 #define RWKV_DISPATCH(LAUNCH, ...)                                                              \
@@ -874,8 +1024,10 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
     const int64_t nCT = (C + kTileChannels - 1) / kTileChannels;
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
-    // words [tiles][4][64] u64 (one published state per tile) + one error word
-    return (size_t)(tiles * 4 * kTileChannels * 8 + 256);
+    // words [tiles][4][64] u64 (one published state per tile, single pass) + one error word
+    // (padded to 256 B) + aggregates [tiles][64][4] fp32 (two passes).  The two regions are
+    // disjoint, so a float left by one algorithm can never pass for a tagged word.
+    return (size_t)(tiles * 4 * kTileChannels * 8 + 256 + tiles * kTileChannels * 4 * 4);
 }
 
 void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
@@ -886,6 +1038,7 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
     char *p = static_cast<char *>(base);
     ws->words = reinterpret_cast<uint64_t *>(p);
     ws->err = reinterpret_cast<uint32_t *>(p + tiles * 4 * kTileChannels * 8);
+    ws->aggs = reinterpret_cast<float *>(p + tiles * 4 * kTileChannels * 8 + 256);
 }
 
 hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATCH(launch_seq_t, a, s); }
@@ -893,6 +1046,11 @@ hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATC
 hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
                           hipStream_t s) {
     RWKV_DISPATCH(launch_chunk_t, a, chunk_len, ws, s);
+}
+
+hipError_t launch_chunked_2pass(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
+                                hipStream_t s) {
+    RWKV_DISPATCH(launch_chunk2_t, a, chunk_len, ws, s);
 }
 
 hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s) {

@@ -80,6 +80,7 @@ def test_bad_opts():
     assert fwd(o=opts(in_dtype=7)) == rw.RWKV_ERR_DTYPE
     assert fwd(o=opts(out_dtype=-1)) == rw.RWKV_ERR_DTYPE
     assert fwd(o=opts(algo=5)) == rw.RWKV_ERR_ARG
+    assert fwd(o=opts(algo=4)) == rw.RWKV_ERR_ARG
     for c in (32, 100, 2048, -64):
         assert fwd(o=opts(chunk_len=c)) == rw.RWKV_ERR_ARG, c
     assert fwd(o=opts(workspace=P + 4, workspace_bytes=1 << 20)) == rw.RWKV_ERR_ALIGN
@@ -158,6 +159,7 @@ def test_workspace_bytes():
     a = rw.rwkv4_workspace_bytes(1, 65536, 2048, 64)
     b = rw.rwkv4_workspace_bytes(1, 65536, 2048, 1024)
     assert a > b > 0
-    # tiles * 4 fields * 64 channels * 8-byte tagged words, plus the error word
+    # tiles * 4 fields * 64 channels * 8-byte tagged words, the error word, and the
+    # two-pass aggregates (tiles * 64 channels * 4 fp32)
     tiles = 32 * 1024
-    assert a == tiles * 4 * 64 * 8 + 256
+    assert a == tiles * 4 * 64 * 8 + 256 + tiles * 64 * 16

@@ -44,7 +44,7 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
     return host(y), (host(so) if so is not None else None)
 
 
-ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("auto", 0)]
+ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128), ("auto", 0)]
 
 
 # ----------------------------------------------------------------------------- small, ragged
@@ -64,7 +64,7 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64)])
 def test_odd_channels(C, algo, chunk):
     # C % 4 != 0 takes the per-element path; C < 64 leaves most of a tile masked
     case = wi.forward_case(3, 300, C, seed=42, in_dtype="f16", gated=True, prior=True)
@@ -74,7 +74,7 @@ def test_odd_channels(C, algo, chunk):
     check_state(st, ref, TOL["f16"], f"C={C} {algo}/{chunk}")
 
 
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("two_pass", 64)])
 def test_misaligned_pointers(algo, chunk):
     """Tensors offset by one element: the library must take the per-element path."""
     import rwkv_wkv_linear_amd as rw
@@ -101,11 +101,11 @@ def test_misaligned_pointers(algo, chunk):
     check_state(host(so), ref, TOL["f16"], f"misaligned {algo}")
 
 
-@pytest.mark.parametrize("algo", ["sequential", "chunked"])
+@pytest.mark.parametrize("algo", ["sequential", "chunked", "two_pass"])
 def test_single_token(algo):
     case = wi.forward_case(4, 1, 96, seed=44, in_dtype="f32", gated=True, prior=True)
     ref = oracle.forward(case, method="direct")
-    y, st = run(case, algo, 64 if algo == "chunked" else 0, label="T=1")
+    y, st = run(case, algo, 0 if algo == "sequential" else 64, label="T=1")
     check_output(y, ref, TOL["f32"], f"T=1 {algo}")
     check_state(st, ref, TOL["f32"], f"T=1 {algo}")
 
@@ -133,7 +133,7 @@ def test_state_in_place_and_null_state():
     t = torch()
     case = wi.forward_case(2, 700, 128, seed=46, in_dtype="f16", gated=True, prior=True)
     ref = oracle_forward("inplace", case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 128)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64)):
         st = to_dev(case["state_in"])
         y = t.empty((2, 700, 128), dtype=t.float16, device="cuda:0")
         note(f"forward in-place state {algo}/{chunk}")
@@ -155,7 +155,7 @@ def test_full_forgetting_channels():
     case["w"] = case["w"].copy()
     case["w"][::3] = -np.inf
     ref = oracle.forward(case, method="direct")
-    for algo, chunk in (("sequential", 0), ("chunked", 64)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, st = run(case, algo, chunk, label="w=-inf")
         check_output(y, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
         check_state(st, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
@@ -171,7 +171,7 @@ def test_shift_invariance_needs_max_trick(shift):
     st[2] = st[2] + shift
     case["state_in"] = st
     ref = oracle.forward(case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, s = run(case, algo, chunk, label=f"shift {shift}")
         check_output(y, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
         check_state(s, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
@@ -183,13 +183,14 @@ def test_wide_key_spread():
     g = np.random.default_rng(49)
     case["k"] = g.uniform(-60, 60, case["k"].shape).astype(np.float32)
     ref = oracle.forward(case)
-    for algo, chunk in (("sequential", 0), ("chunked", 64)):
+    for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, s = run(case, algo, chunk, label="wide spread")
         check_output(y, ref, TOL["f32"], f"spread {algo}/{chunk}")
         check_state(s, ref, TOL["f32"], f"spread {algo}/{chunk}")
 
 
-def test_split_sequence_carry():
+@pytest.mark.parametrize("algo", ["chunked", "two_pass"])
+def test_split_sequence_carry(algo):
     import rwkv_wkv_linear_amd as rw
     t = torch()
     case = wi.forward_case(2, 900, 128, seed=50, in_dtype="f32", gated=True, prior=True)
@@ -198,28 +199,29 @@ def test_split_sequence_carry():
     dk, dv, dr = to_dev(case["k"]), to_dev(case["v"]), to_dev(case["r"])
     w, u = to_dev(case["w"]), to_dev(case["u"])
     st = to_dev(case["state_in"])
-    note("forward split carry")
+    note(f"forward split carry {algo}")
     y1 = rw.rwkv4_wkv_forward(dk[:, :T1].contiguous(), dv[:, :T1].contiguous(), w, u, state_in=st,
-                              state_out=st, r=dr[:, :T1].contiguous(), algo="chunked", chunk_len=64)
+                              state_out=st, r=dr[:, :T1].contiguous(), algo=algo, chunk_len=64)
     y2 = rw.rwkv4_wkv_forward(dk[:, T1:].contiguous(), dv[:, T1:].contiguous(), w, u, state_in=st,
-                              state_out=st, r=dr[:, T1:].contiguous(), algo="chunked", chunk_len=64)
+                              state_out=st, r=dr[:, T1:].contiguous(), algo=algo, chunk_len=64)
     t.cuda.synchronize()
     y = np.concatenate([host(y1), host(y2)], axis=1)
-    check_output(y, ref, TOL["f32"], "split carry")
-    check_state(host(st), ref, TOL["f32"], "split carry")
+    check_output(y, ref, TOL["f32"], f"split carry {algo}")
+    check_state(host(st), ref, TOL["f32"], f"split carry {algo}")
 
 
-def test_deterministic():
+@pytest.mark.parametrize("algo", ["chunked", "two_pass"])
+def test_deterministic(algo):
     import rwkv_wkv_linear_amd as rw
     t = torch()
     case = wi.forward_case(2, 2048, 256, seed=51, in_dtype="f16", gated=True, prior=True)
     args = [to_dev(case[n]) for n in ("k", "v", "w", "u")]
     outs = []
     for _ in range(2):
-        note("forward determinism")
+        note(f"forward determinism {algo}")
         so = t.empty((3, 2, 256), device="cuda:0")
         y = rw.rwkv4_wkv_forward(*args, state_in=to_dev(case["state_in"]), state_out=so,
-                                 r=to_dev(case["r"]), algo="chunked", chunk_len=64)
+                                 r=to_dev(case["r"]), algo=algo, chunk_len=64)
         t.cuda.synchronize()
         outs.append((y.clone(), so.clone()))
     assert t.equal(outs[0][0], outs[1][0]) and t.equal(outs[0][1], outs[1][1])

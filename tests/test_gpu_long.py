@@ -42,3 +42,23 @@ def test_long_sequence_chunk_sweep(chunk):
     t.cuda.synchronize()
     check_output(host(y), ref, TOL["f16"], f"long chunk={chunk}")
     check_state(host(so), ref, TOL["f16"], f"long chunk={chunk}")
+
+
+@pytest.mark.parametrize("T,chunk", [(4096, 64), (6400, 64), (8192, 128)])
+def test_two_pass_long_chains(T, chunk):
+    """The two-pass scan on chains of 64 to 100 tiles: each wave folds its share of the
+    predecessors' aggregates in several batches."""
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    case = wi.forward_case(2, T, 256, seed=61, in_dtype="f16", out_dtype="f32", k_sigma=np.sqrt(2.0),
+                           prior=True, index=4)
+    ref = oracle.forward(case)
+    y = t.full((2, T, 256), float("nan"), dtype=t.float32, device="cuda:0")
+    so = t.full((3, 2, 256), float("nan"), device="cuda:0")
+    note(f"two-pass forward B=2 T={T} C=256 chunk={chunk}")
+    rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]), y=y,
+                         state_in=to_dev(case["state_in"]), state_out=so, out_dtype=t.float32,
+                         algo="two_pass", chunk_len=chunk)
+    t.cuda.synchronize()
+    check_output(host(y), ref, TOL["f16"], f"two-pass T={T} chunk={chunk}", out_dtype="f32")
+    check_state(host(so), ref, TOL["f16"], f"two-pass T={T} chunk={chunk}")

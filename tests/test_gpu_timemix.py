@@ -60,7 +60,7 @@ def check_all(out, ref, case, what, with_xkv):
             note(f"{what}: {name} max |err| - bound = {excess:.3e}")
             assert excess <= 0, f"{what}: {name} off by more than half an ulp"
 
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)])
 @pytest.mark.parametrize("with_xkv", [False, True])
 def test_ragged_prior(algo, chunk, with_xkv):
     case = wi.timemix_case(2, 777, 136, seed=61, prior=True)
@@ -71,7 +71,7 @@ def test_ragged_prior(algo, chunk, with_xkv):
     check_all(out, _cache[key], case, f"timemix ragged {algo}/{chunk}", with_xkv)
 
 
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("two_pass", 64)])
 def test_fp32_odd_channels_no_prev(algo, chunk):
     case = wi.timemix_case(1, 300, 37, seed=62, in_dtype="f32", prior=True)
     nop = dict(case, x_prev=np.zeros_like(case["x_prev"]))
@@ -96,7 +96,7 @@ def test_zero_tokens():
     assert np.array_equal(host(so), case["state_in"].astype(np.float64))
 
 
-@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("sequential", 0), ("chunked", 64), ("chunked", 128)])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)])
 def test_workload_14b_layer(algo, chunk):
     """B1 T1024 C5120 fp16, token shift from x_prev, r = xr, y = sigmoid(xr) wkv (fp16)."""
     case = wi.workload_inputs(2)
