@@ -420,7 +420,7 @@ __device__ __forceinline__ void stage_rows(const TIn *const *src, TIn *rows, int
 // (whether the linear-space guard holds; else the exact per-token max-trick ran).
 template <typename TIn, int L>
 __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nval, float wc, float uc, float ew,
-                                           float &kmax, bool &fast) {
+                                           float &kmax, bool &fast, float (&Xs)[L]) {
     constexpr int CW = kTileChannels;
     kmax = -INFINITY;
     float kmin = INFINITY;
@@ -451,6 +451,7 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 const float X = ex(xk[i] - kmax);
+                Xs[i] = X;  // kept for the emit phase
                 nn = fmaf(ew, nn, X * vb[i]);
                 dd = fmaf(ew, dd, X);
             }
@@ -478,9 +479,10 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
 // nn <- e^w nn + P, dd <- e^w dd + X.  The optional writes are template switches so the
 // unrolled loop has no branches: STAGE puts y in the wave's LDS v rows (each row is read
 // into registers before it is overwritten; the caller then writes 16 bytes per lane), MIX
-// writes the time-mix xk/xv rows.  kr, vr, gr point at the lane's first staged row.
+// writes the time-mix xk/xv rows.  Xs holds the weights e^{k_i - kmax} from the summary
+// phase; vr, gr point at the lane's first staged row.
 template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
-__device__ __forceinline__ void emit_full(const TIn *kr, const TIn *vr, const TIn *gr, float kmax, float eu,
+__device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, const TIn *gr, float eu,
                                           float ew, float ga, float gb, float mk, float mv, float &xs, float &nn,
                                           float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
                                           unsigned Cu, int lane) {
@@ -491,17 +493,16 @@ __device__ __forceinline__ void emit_full(const TIn *kr, const TIn *vr, const TI
     float gbx = gb * xs;  // the gate's previous-token term
 #pragma unroll
     for (int h = 0; h < L; h += LB) {
-        TIn kh[LB], vh[LB], gh[LB];
+        TIn vh[LB], gh[LB];
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
-            kh[j] = kr[(h + j) * CW];
             vh[j] = vr[(h + j) * CW];
             gh[j] = (MODE == MODE_PLAIN) ? TIn(0) : gr[(h + j) * CW];
         }
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             const int i = h + j;
-            const float X = ex((float)kh[j] - kmax);  // e^{k_i - kmax}, subtracted first: exact for large keys
+            const float X = Xs[i];  // e^{k_i - kmax} from the summary phase
             const float P = fmaf(X, (float)vh[j], 0.f);
             const float num = fmaf(eu, P, nn);
             const float den = fmaf(eu, X, dd);
@@ -541,11 +542,12 @@ __device__ __forceinline__ void emit_full(const TIn *kr, const TIn *vr, const TI
 // only for its own rows.  Only the weights X_i stay in VGPRs.  When the pointers are not
 // 16-byte aligned or C is not a multiple of a 16-byte chunk, each lane loads its own
 // channel instead (same LDS layout).  Rows past T and chunks past C read a valid address
-// whose data is never used.  The weights X_i are recomputed from the staged keys in
-// phase E rather than held in VGPRs across the look-back, which keeps the register
-// footprint low enough for every workgroup of a layer-sized call to be resident at once.
+// whose data is never used.  A full wave keeps its weights X_i from phase B to phase E
+// (saving an exponential per token); amdgpu_waves_per_eu(5) holds the kernel to 96 VGPRs,
+// so with 28 KB of LDS five workgroups share a CU and every workgroup of a layer-sized
+// call is resident at once.
 template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
     constexpr int CW = kTileChannels;
     constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
@@ -666,7 +668,8 @@ __global__ void __launch_bounds__(1024)
     // Phase B: summary of the wave's tokens from the empty state.
     float kmax;
     bool fast;
-    const St sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast);
+    float Xs[L];  // the weights e^{k_i - kmax} of a full wave on the fast path
+    const St sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
@@ -749,7 +752,7 @@ __global__ void __launch_bounds__(1024)
             TOut *yrow = Y + row0;
             TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
 #define RWKV_EMIT(STAGE, MIX)                                                                          \
-    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(kr, vr, gr, kmax, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
+    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow,       \
                                               xkrow, xvrow, ystage, Cu, lane)
             if constexpr (MODE == MODE_TIMEMIX) {
                 if (stage_y) {
@@ -851,7 +854,7 @@ __global__ void __launch_bounds__(1024)
 // time tile but the last of each chain, written as one float4 (a, b, key, age) per (tile,
 // channel) to ws.aggs.  Same tiling and phases A-B as wkv_tile_kernel, on k and v only.
 template <typename TIn, int L>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     wkv_tile_agg_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW) {
     constexpr int CW = kTileChannels;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -878,8 +881,9 @@ __global__ void __launch_bounds__(1024)
     __builtin_amdgcn_wave_barrier();
     float kmax;
     bool fast;
+    float Xs[L];
     const St sum = wave_summary<TIn, L>(rows + (size_t)wv * L * CW + lane, rows + ((size_t)TW + wv * L) * CW + lane,
-                                        cok ? L : 0, wc, uc, ew, kmax, fast);
+                                        cok ? L : 0, wc, uc, ew, kmax, fast, Xs);
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
