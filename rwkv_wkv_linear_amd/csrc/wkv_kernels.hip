@@ -533,13 +533,14 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 
 // Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = S * L tokens),
 // blockIdx = tt * (B * nCT) + b * nCT + ct, so every tile a workgroup waits for has a
-// lower index and was dispatched earlier.  Wave w of S = tokens tt*TW + w*L .. +L-1;
+// lower index and was dispatched earlier.  PREFIX selects where the tile's incoming state
+// comes from: the single-pass look-back (phase D) or the aggregates of a first pass.  Wave w of S = tokens tt*TW + w*L .. +L-1;
 // lane = channel ct*64 + lane.
 //
 // The tile's rows of k, v (and r or x) are staged in LDS as [tensor][TW][64] by 16-byte
 // global-to-LDS loads (global_load_lds_dwordx4): each wave fetches the L rows it computes
 // on, 8 rows of 128 B per instruction, so no VGPR holds a load in flight and a wave waits
-// only for its own rows.  Only the weights X_i stay in VGPRs.  When the pointers are not
+// only for its own rows.  When the pointers are not
 // 16-byte aligned or C is not a multiple of a 16-byte chunk, each lane loads its own
 // channel instead (same LDS layout).  Rows past T and chunks past C read a valid address
 // whose data is never used.  A full wave keeps its weights X_i from phase B to phase E
