@@ -174,6 +174,10 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
     a.vec16y = (a.y && aligned(a.y, 16) && (C % (int64_t)(16 / eo)) == 0) ? 1 : 0;
     a.vecs = ((C % 4) == 0 && (!a.state_in || aligned(a.state_in, 16)) &&
               (!a.state_out || aligned(a.state_out, 16))) ? 1 : 0;
+    bool vecp = (C % 4) == 0;
+    for (const float *p : {a.w, a.u, a.mix_k, a.mix_v, a.mix_r})
+        if (p && !aligned(p, 16)) vecp = false;
+    a.vecp = vecp ? 1 : 0;
 
     hipError_t e;
     if (T == 0) {

@@ -32,6 +32,7 @@ struct ForwardArgs {
     int vec16;   // 1: input rows split into 16-byte chunks (C % (16 / size) == 0, 16-B aligned)
     int vec16y;  // 1: the same for y
     int vecs;    // 1: C % 4 == 0 and both state pointers 16-byte aligned (float4 state I/O)
+    int vecp;    // 1: C % 4 == 0 and every per-channel parameter pointer 16-byte aligned
 };
 
 // Chunked-scan scratch: per tile and channel four 64-bit words (a, b, key, age), each the

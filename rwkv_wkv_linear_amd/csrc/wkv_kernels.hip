@@ -153,7 +153,14 @@ template <typename T, int L> struct Rows {
     __device__ __forceinline__ float get(int i) const { return (float)p[i]; }
 };
 
-__device__ __forceinline__ void load_param4(const float *p, int64_t c0, int nch, float (&x)[4]) {
+// Four per-channel parameters c0 .. c0+3 (zeros past C); one 16-byte load when aligned.
+__device__ __forceinline__ void load_param4(const float *p, int64_t c0, int nch, bool vec, float (&x)[4]) {
+    if (vec && nch == 4) {
+        const f4 v = *reinterpret_cast<const f4 *>(p + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = v[q];
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) x[q] = (q < nch) ? p[c0 + q] : 0.f;
 }
@@ -177,8 +184,9 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
     TOut *Y = static_cast<TOut *>(a.y);
 
     float w[4], u[4];
-    load_param4(a.w, c0, nch, w);
-    load_param4(a.u, c0, nch, u);
+    const bool vp = a.vecp != 0;
+    load_param4(a.w, c0, nch, vp, w);
+    load_param4(a.u, c0, nch, vp, u);
     St s[4];
     const bool vs = a.vecs != 0 && nch == 4;  // the lane's state is three aligned float4
 #pragma unroll
@@ -199,9 +207,9 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
     }
     float mk[4], mv[4], mr[4], xs[4];
     if constexpr (MODE == MODE_TIMEMIX) {
-        load_param4(a.mix_k, c0, nch, mk);
-        load_param4(a.mix_v, c0, nch, mv);
-        load_param4(a.mix_r, c0, nch, mr);
+        load_param4(a.mix_k, c0, nch, vp, mk);
+        load_param4(a.mix_v, c0, nch, vp, mv);
+        load_param4(a.mix_r, c0, nch, vp, mr);
         const TIn *XP = static_cast<const TIn *>(a.x_prev);
         auto xp = XP ? load4(XP, sc, nch, vec) : typename Raw<TIn>::type{0, 0, 0, 0};
 #pragma unroll
