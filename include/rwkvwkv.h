@@ -92,7 +92,8 @@ typedef struct rwkv4_opts {
     int32_t out_dtype;       /* rwkv_dtype of y */
     const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
-    int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto,
+    int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (64,
+                                or 128 for fp16 inputs with more than 64 tiles of 64),
                                 else 64 or 128 (fp16) / 64 (fp32): the tile's rows
                                 are staged in the workgroup's LDS */
     int32_t algo;            /* rwkv_algo */
@@ -164,7 +165,8 @@ const char *rwkv_status_string(rwkv_status s);
 /* Thread-local message for the last non-OK return on this thread ("" if none). */
 const char *rwkv_last_error(void);
 
-/* Bytes of workspace the chunked scan needs for this shape (chunk_len 0 = auto). */
+/* Bytes of workspace the chunked scans need for this shape (chunk_len 0: enough for the
+   automatic tile length of either input dtype). */
 size_t rwkv4_workspace_bytes(int64_t B, int64_t T, int64_t C, int32_t chunk_len);
 
 /* RWKV_ABI_VERSION of the loaded library. */

@@ -191,7 +191,7 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         if (e != hipSuccess) return hip_fail(e, "launch (sequential)");
         return ok();
     }
-    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C);
+    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, a.in_f16);
     const int cmax = chunk_max_len(a.in_f16, a.mode);
     if (chunk > cmax) {
         if (o.chunk_len)
@@ -335,7 +335,9 @@ const char *rwkv_last_error(void) { return g_err; }
 
 size_t rwkv4_workspace_bytes(int64_t B, int64_t T, int64_t C, int32_t chunk_len) {
     if (B < 1 || C < 1 || T < 1) return 0;
-    int chunk = chunk_len > 0 ? chunk_len : auto_chunk_len(B, T, C);
+    // chunk_len 0: the size for the automatic choice whatever the dtype (64-token tiles, the
+    // largest workspace; fp16 long sequences may then use 128-token tiles and need less)
+    int chunk = chunk_len > 0 ? chunk_len : auto_chunk_len(B, T, C, 0);
     if (T <= chunk) return 0;
     return chunk_workspace_bytes(B, T, C, chunk);
 }

@@ -50,7 +50,7 @@ constexpr int kMinChunk = 64, kMaxChunk = 1024;
 // Largest chunk length the chunked kernel supports for a dtype/mode (its register budget).
 int chunk_max_len(int in_f16, int mode);
 // Chunk length (tokens per workgroup tile) the auto policy picks for a shape.
-int auto_chunk_len(int64_t B, int64_t T, int64_t C);
+int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_f16);
 // True when the auto policy picks the sequential kernel.
 bool auto_sequential(int64_t B, int64_t T, int64_t C);
 // Workspace layout for a chunked launch.
