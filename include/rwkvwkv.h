@@ -92,10 +92,10 @@ typedef struct rwkv4_opts {
     int32_t out_dtype;       /* rwkv_dtype of y */
     const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
-    int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (64,
-                                or 128 for fp16 inputs with more than 64 tiles of 64),
-                                else 64 or 128 (fp16) / 64 (fp32): the tile's rows
-                                are staged in the workgroup's LDS */
+    int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (128
+                                for fp16 inputs, 64 for fp32), else 64 or 128 (fp16) /
+                                64 (fp32): the tile's rows are staged in the
+                                workgroup's LDS */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
                                 else device memory of workspace_bytes >= the size

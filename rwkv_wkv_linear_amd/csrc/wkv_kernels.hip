@@ -556,8 +556,8 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 // so with 28 KB of LDS five workgroups share a CU and every workgroup of a layer-sized
 // call is resident at once.
 template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
-    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
+__device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorkspace &ws, int S, int nCT, int nTT,
+                                          int TW, int M) {
     constexpr int CW = kTileChannels;
     constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -857,6 +857,23 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     }
 }
 
+// 16 tokens per wave (chunk_len = 16 * waves): 96 VGPRs so that five 4-wave workgroups
+// share a CU.
+template <typename TIn, typename TOut, int MODE, int PREFIX>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
+    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
+    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M);
+}
+
+// 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
+// quarter of the look-back reads; three 52 KB workgroups share a CU, and with that
+// occupancy each wave may hold its 32 weights in registers.
+template <typename TIn, typename TOut, int MODE, int PREFIX>
+__global__ void __launch_bounds__(256)
+    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
+    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M);
+}
+
 // ------------------------------------------------------------------------------------------
 
 // First pass of the two-pass scan: the aggregate (summary from the empty state) of every
@@ -973,18 +990,27 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, L, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                       a, ws, S, nCT, nTT, chunk_len, M);
+    if constexpr (L == 32)
+        hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
+                           a, ws, S, nCT, nTT, chunk_len, M);
+    else
+        hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
+                           a, ws, S, nCT, nTT, chunk_len, M);
     return hipGetLastError();
 }
 
+// 64-token tiles: 4 waves of 16 tokens; 128-token tiles: 4 waves of 32 tokens.
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    if constexpr (sizeof(TIn) == 2)
+        if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
 }
 
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    if constexpr (sizeof(TIn) == 2)
+        if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_AGGS>(a, chunk_len, ws, s);
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
 }
 
@@ -1028,12 +1054,12 @@ bool auto_sequential(int64_t B, int64_t T, int64_t C) {
 int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_f16) {
     (void)B;
     (void)C;
-    // 64-token tiles (4 waves of 16 tokens) keep the look-back short and every workgroup of
-    // a layer-sized call resident.  Long chains (more than 64 such tiles) run many rounds of
-    // workgroups and are bound by workgroups in flight x their latency; fp16 tiles of 128
-    // tokens (8 waves) measured 8 % faster there (B1 T65536 C2048: 386 -> 355 us).
-    const int64_t tiles64 = (T + kMinChunk - 1) / kMinChunk;
-    return (in_f16 && tiles64 > 64) ? 2 * kMinChunk : kMinChunk;
+    (void)T;
+    // fp16: 128-token tiles of 4 waves x 32 tokens.  Against 64-token tiles (4 x 16) they halve
+    // the tiles per chain and quarter the look-back reads, and three 52 KB workgroups per CU
+    // still hold a layer-sized call at once: 14B layer 18.2 -> 17.3 us, 169m batch 20.6 ->
+    // 18.1 us, B1 T65536 C2048 386 -> 286 us.  fp32 rows are twice the size: 64 tokens.
+    return in_f16 ? 2 * kMinChunk : kMinChunk;
 }
 
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
