@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "two_pass", "sequential"])
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode14b: capture the 40 layers' launches into one HIP graph and replay it "
+                         "per step")
     ap.add_argument("--copy-kernel", action="store_true",
                     help="time a plain device-to-device copy instead (counter calibration)")
     ap.add_argument("--copy-mib", type=float, default=256.0)
@@ -283,6 +286,30 @@ def main():
     for i in range(W):
         su.step(i, rw)
     torch.cuda.synchronize()
+    step = su.step
+    if args.graph:
+        if name != "decode14b":
+            print("--graph applies to --workload decode14b", file=sys.stderr, flush=True)
+            sys.exit(2)
+        # the 40 step launches captured once over the same buffers; a replay is one step
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(su.stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph):
+                cap = torch.cuda.current_stream().cuda_stream
+                for call in su.sets[0]:
+                    st = su.fn(*call[:-1], ctypes.c_void_p(cap))
+                    if st != 0:
+                        raise rw.RwkvError(st, rw.rwkv_last_error())
+        su.stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+        def step(i, rw_):
+            graph.replay()
 
     # The timed region: K steps launched back to back on the stream, bracketed by one pair
     # of HIP events on that stream and by device synchronisations.  A timing event between
@@ -294,7 +321,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(su.stream)
     for i in range(K):
-        su.step(W + i, rw)
+        step(W + i, rw)
     ev1.record(su.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -319,7 +346,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": su.desc, "B": su.B, "T": su.T, "C": su.C, "io_dtype": su.io,
                    "entry_point": su.entry, "launches_per_step": su.launches_per_step,
-                   "algo": args.algo, "chunk_len": chunk, "rotated_sets": len(su.sets)},
+                   "algo": args.algo, "chunk_len": chunk, "rotated_sets": len(su.sets),
+                   "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel_avg_us": launch_avg_ms * 1e3,
