@@ -68,7 +68,10 @@ typedef enum rwkv_status {
     RWKV_ERR_NOMEM = -5   /* the library-cached workspace could not be allocated */
 } rwkv_status;
 
-typedef enum rwkv_dtype { RWKV_F32 = 0, RWKV_F16 = 1 } rwkv_dtype;
+/* Element types of activations.  BF16 (bfloat16: fp32's exponent, 8 significand bits) is
+   converted to fp32 on load and rounded to nearest-even on store, like F16; the recurrence
+   and the state are always fp32. */
+typedef enum rwkv_dtype { RWKV_F32 = 0, RWKV_F16 = 1, RWKV_BF16 = 2 } rwkv_dtype;
 
 typedef enum rwkv_algo {
     RWKV_ALGO_AUTO = 0,        /* pick by shape: sequential for large B*C (or T <= 1), else
@@ -93,9 +96,9 @@ typedef struct rwkv4_opts {
     const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
     int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (128
-                                for fp16 inputs, 64 for fp32), else 64 or 128 (fp16) /
-                                64 (fp32): the tile's rows are staged in the
-                                workgroup's LDS */
+                                for 2-byte inputs (fp16, bf16), 64 for fp32), else 64 or
+                                128 (2-byte) / 64 (fp32): the tile's rows are staged in
+                                the workgroup's LDS */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
                                 else device memory of workspace_bytes >= the size

@@ -21,7 +21,7 @@ from __future__ import annotations
 import numpy as np
 
 
-FLOOR = {"f32": 0.0, "f16": 2.0 ** -14}
+FLOOR = {"f32": 0.0, "f16": 2.0 ** -14, "bf16": 0.0}  # bf16 has fp32's exponent range
 
 
 def scaled_error(y, y_ref, scale_ref, floor=0.0):

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "librwkvwkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "rwkvwkv.h")
 
 RWKV_OK, RWKV_ERR_ARG, RWKV_ERR_DTYPE, RWKV_ERR_ALIGN, RWKV_ERR_HIP, RWKV_ERR_NOMEM = 0, -1, -2, -3, -4, -5
-RWKV_F32, RWKV_F16 = 0, 1
+RWKV_F32, RWKV_F16, RWKV_BF16 = 0, 1, 2
 RWKV_ALGO_AUTO, RWKV_ALGO_SEQUENTIAL, RWKV_ALGO_CHUNKED, RWKV_ALGO_TWO_PASS = 0, 1, 2, 3
 _ALGOS = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3, 0: 0, 1: 1, 2: 2, 3: 3}
 
@@ -135,7 +135,9 @@ def _dtype_code(dt):
         return RWKV_F32
     if dt == torch.float16:
         return RWKV_F16
-    raise TypeError(f"unsupported dtype {dt}: float32 or float16")
+    if dt == torch.bfloat16:
+        return RWKV_BF16
+    raise TypeError(f"unsupported dtype {dt}: float32, float16 or bfloat16")
 
 
 def _ptr(t):
@@ -188,7 +190,7 @@ def _opts(in_dtype, out_dtype, r=None, chunk_len=0, algo="auto", workspace=None)
 def rwkv4_wkv_forward(k, v, w, u, y=None, state_in=None, state_out=None, *, r=None, out_dtype=None,
                       chunk_len=0, algo="auto", workspace=None, stream=None):
     """y = WKV(k, v) (or sigmoid(r) * WKV when r is given); fills state_out if given.
-    k, v, r: [B, T, C] float16/float32; w, u: [C] float32; states: [3, B, C] float32."""
+    k, v, r: [B, T, C] float32/float16/bfloat16; w, u: [C] float32; states: [3, B, C] float32."""
     torch = _torch()
     B, T, C = k.shape
     dev = k.device

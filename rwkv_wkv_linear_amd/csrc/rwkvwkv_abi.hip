@@ -90,11 +90,12 @@ bool overlap(const void *p, size_t pn, const void *q, size_t qn) {
 const int64_t kMaxElems = (int64_t)1 << 46;
 
 rwkv_status check_dtype(int32_t d, const char *what) {
-    if (d != RWKV_F32 && d != RWKV_F16) return fail(RWKV_ERR_DTYPE, "%s: unknown dtype %d", what, (int)d);
+    if (d != RWKV_F32 && d != RWKV_F16 && d != RWKV_BF16)
+        return fail(RWKV_ERR_DTYPE, "%s: unknown dtype %d", what, (int)d);
     return RWKV_OK;
 }
 
-size_t esize(int32_t d) { return d == RWKV_F16 ? 2 : 4; }
+size_t esize(int32_t d) { return d == RWKV_F32 ? 4 : 2; }
 
 struct Resolved {
     int32_t in_dtype = RWKV_F32, out_dtype = RWKV_F32;
@@ -160,8 +161,8 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
     if (a.state_out && (overlap(a.state_out, sbytes, a.y, abytes_out)))
         return fail(RWKV_ERR_ARG, "state_out overlaps y");
 
-    a.in_f16 = o.in_dtype == RWKV_F16;
-    a.out_f16 = o.out_dtype == RWKV_F16;
+    a.in_dt = o.in_dtype;
+    a.out_dt = o.out_dtype;
     bool vec = (C % 4) == 0;
     for (const void *p : ins)
         if (p && !aligned(p, 4 * ei)) vec = false;
@@ -191,8 +192,8 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         if (e != hipSuccess) return hip_fail(e, "launch (sequential)");
         return ok();
     }
-    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, a.in_f16);
-    const int cmax = chunk_max_len(a.in_f16, a.mode);
+    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, ei == 2);
+    const int cmax = chunk_max_len(ei == 2, a.mode);
     if (chunk > cmax) {
         if (o.chunk_len)
             return fail(RWKV_ERR_ARG, "chunk_len %d exceeds %d, the largest tile this dtype/mode supports",

@@ -26,7 +26,7 @@ struct ForwardArgs {
     void *y;
     const float *state_in;  // may be null (empty state)
     float *state_out;       // may be null
-    int in_f16, out_f16;
+    int in_dt, out_dt;  // rwkv_dtype codes: 0 fp32, 1 fp16, 2 bf16
     int mode;
     int vec;    // 1: C % 4 == 0 and activation pointers aligned for 4-element vectors
     int vec16;   // 1: input rows split into 16-byte chunks (C % (16 / size) == 0, 16-B aligned)
@@ -48,9 +48,9 @@ constexpr int kTileChannels = 64;  // channels per workgroup tile
 constexpr int kMinChunk = 64, kMaxChunk = 1024;
 
 // Largest chunk length the chunked kernel supports for a dtype/mode (its register budget).
-int chunk_max_len(int in_f16, int mode);
+int chunk_max_len(int in_2byte, int mode);
 // Chunk length (tokens per workgroup tile) the auto policy picks for a shape.
-int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_f16);
+int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_2byte);
 // True when the auto policy picks the sequential kernel.
 bool auto_sequential(int64_t B, int64_t T, int64_t C);
 // Workspace layout for a chunked launch.

@@ -44,6 +44,7 @@ namespace rwkvwkv {
 namespace {
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -55,6 +56,7 @@ constexpr int kMaxAnchorGap = 16;         // spacing of anchor tiles in a chain 
 template <typename T> struct Raw;
 template <> struct Raw<float> { using type = f4; };
 template <> struct Raw<_Float16> { using type = h4; };
+template <> struct Raw<__bf16> { using type = b4; };
 
 __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -1014,34 +1016,32 @@ hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorks
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
 }
 
-#define RWKV_DISPATCH(LAUNCH, ...)                                                              \
-    do {                                                                                        \
-        if (a.in_f16) {                                                                         \
-            if (a.out_f16) {                                                                    \
-                if (a.mode == MODE_PLAIN) return LAUNCH<_Float16, _Float16, MODE_PLAIN>(__VA_ARGS__); \
-                if (a.mode == MODE_GATED) return LAUNCH<_Float16, _Float16, MODE_GATED>(__VA_ARGS__); \
-                return LAUNCH<_Float16, _Float16, MODE_TIMEMIX>(__VA_ARGS__);                   \
-            }                                                                                   \
-            if (a.mode == MODE_PLAIN) return LAUNCH<_Float16, float, MODE_PLAIN>(__VA_ARGS__);  \
-            if (a.mode == MODE_GATED) return LAUNCH<_Float16, float, MODE_GATED>(__VA_ARGS__);  \
-            return LAUNCH<_Float16, float, MODE_TIMEMIX>(__VA_ARGS__);                          \
-        }                                                                                       \
-        if (a.out_f16) {                                                                        \
-            if (a.mode == MODE_PLAIN) return LAUNCH<float, _Float16, MODE_PLAIN>(__VA_ARGS__);  \
-            if (a.mode == MODE_GATED) return LAUNCH<float, _Float16, MODE_GATED>(__VA_ARGS__);  \
-            return LAUNCH<float, _Float16, MODE_TIMEMIX>(__VA_ARGS__);                          \
-        }                                                                                       \
-        if (a.mode == MODE_PLAIN) return LAUNCH<float, float, MODE_PLAIN>(__VA_ARGS__);         \
-        if (a.mode == MODE_GATED) return LAUNCH<float, float, MODE_GATED>(__VA_ARGS__);         \
-        return LAUNCH<float, float, MODE_TIMEMIX>(__VA_ARGS__);                                 \
+// Every (input dtype, output dtype, mode) instantiation; rwkv_dtype codes 0 fp32, 1 fp16, 2 bf16.
+#define RWKV_DISPATCH_MODE(LAUNCH, TI, TO, ...)                                      \
+    do {                                                                             \
+        if (a.mode == MODE_PLAIN) return LAUNCH<TI, TO, MODE_PLAIN>(__VA_ARGS__);   \
+        if (a.mode == MODE_GATED) return LAUNCH<TI, TO, MODE_GATED>(__VA_ARGS__);   \
+        return LAUNCH<TI, TO, MODE_TIMEMIX>(__VA_ARGS__);                            \
+    } while (0)
+#define RWKV_DISPATCH_OUT(LAUNCH, TI, ...)                                           \
+    do {                                                                             \
+        if (a.out_dt == 1) RWKV_DISPATCH_MODE(LAUNCH, TI, _Float16, __VA_ARGS__);    \
+        if (a.out_dt == 2) RWKV_DISPATCH_MODE(LAUNCH, TI, __bf16, __VA_ARGS__);      \
+        RWKV_DISPATCH_MODE(LAUNCH, TI, float, __VA_ARGS__);                          \
+    } while (0)
+#define RWKV_DISPATCH(LAUNCH, ...)                                                   \
+    do {                                                                             \
+        if (a.in_dt == 1) RWKV_DISPATCH_OUT(LAUNCH, _Float16, __VA_ARGS__);          \
+        if (a.in_dt == 2) RWKV_DISPATCH_OUT(LAUNCH, __bf16, __VA_ARGS__);            \
+        RWKV_DISPATCH_OUT(LAUNCH, float, __VA_ARGS__);                               \
     } while (0)
 
 }  // namespace
 
 // Longest tile per dtype: the tile's rows are staged in LDS (64 KB per workgroup).
-int chunk_max_len(int in_f16, int mode) {
+int chunk_max_len(int in_2byte, int mode) {
     (void)mode;
-    return in_f16 ? 128 : 64;
+    return in_2byte ? 128 : 64;
 }
 
 bool auto_sequential(int64_t B, int64_t T, int64_t C) {
@@ -1051,15 +1051,15 @@ bool auto_sequential(int64_t B, int64_t T, int64_t C) {
     return lanes >= 131072 || T <= 1;
 }
 
-int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_f16) {
+int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_2byte) {
     (void)B;
     (void)C;
     (void)T;
-    // fp16: 128-token tiles of 4 waves x 32 tokens.  Against 64-token tiles (4 x 16) they halve
+    // 2-byte inputs (fp16, bf16): 128-token tiles of 4 waves x 32 tokens.  Against 64-token tiles (4 x 16) they halve
     // the tiles per chain and quarter the look-back reads, and three 52 KB workgroups per CU
     // still hold a layer-sized call at once: 14B layer 18.2 -> 17.3 us, 169m batch 20.6 ->
     // 18.1 us, B1 T65536 C2048 386 -> 286 us.  fp32 rows are twice the size: 64 tokens.
-    return in_f16 ? 2 * kMinChunk : kMinChunk;
+    return in_2byte ? 2 * kMinChunk : kMinChunk;
 }
 
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
@@ -1099,8 +1099,10 @@ hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s) {
     const int64_t n = a.B * a.C;
     const int64_t blocks = (n + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (a.in_f16)
+    if (a.in_dt == 1)
         hipLaunchKernelGGL((wkv_passthrough_kernel<_Float16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else if (a.in_dt == 2)
+        hipLaunchKernelGGL((wkv_passthrough_kernel<__bf16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((wkv_passthrough_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();

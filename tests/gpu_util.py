@@ -8,12 +8,22 @@ import numpy as np
 
 from oracle import compare as cmp
 
-TOL = {"f32": 1e-5, "f16": 2e-3}   # scaled error bar of the outputs, per input dtype
+# Scaled error bar of the outputs, per input dtype.  The oracle reads the rounded inputs, so a
+# 2-byte input costs nothing by itself: bfloat16 inputs take fp16's bar.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+# A bfloat16 output alone rounds by up to half an ulp, 2^-8 relative (8 significand bits), of
+# |y| <= S; its bar is twice that, whatever the input dtype.
+OUT_TOL = {"f32": 0.0, "f16": 0.0, "bf16": 8e-3}
+
+
+def tol_for(in_dtype: str, out_dtype: str) -> float:
+    return max(TOL[in_dtype], OUT_TOL[out_dtype])
 # The fp32 state has no numerator/denominator cancellation: rounding accumulates over the
 # decay window, 1 / (1 - e^w) ~ 149 tokens for the slowest channel (w = -e^-5), at about
 # 4 roundings of 2^-24 per token -> 3.6e-5.  The state bar is this bound, rounded up.
 STATE_TOL_FLOOR = 5e-5
 CANARY = 4096                       # elements after each output that must stay untouched
+CANARY_VALUE = 1232.0               # exact in fp32, fp16 and bfloat16 (7 significant bits)
 
 
 def note(msg: str):
@@ -30,13 +40,16 @@ def dev():
     return torch().device("cuda:0")
 
 
-def to_dev(a):
+def to_dev(a, dtype_name=None):
+    """numpy -> device tensor; dtype_name "bf16" converts the (bfloat16-valued) float32 data
+    to torch.bfloat16, which is exact."""
     if a is None:
         return None
-    return torch().from_numpy(np.ascontiguousarray(a)).to(dev())
+    t = torch().from_numpy(np.ascontiguousarray(a)).to(dev())
+    return t.to(tdtype(dtype_name)) if dtype_name == "bf16" else t
 
 
-_TDT = {"f32": "float32", "f16": "float16"}
+_TDT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
 
 def tdtype(name):
@@ -50,13 +63,13 @@ def poisoned(shape, dtype_name):
     n = int(np.prod(shape))
     full = t.full((n + CANARY,), float("nan"), dtype=tdtype(dtype_name) if isinstance(dtype_name, str)
                   else dtype_name, device=dev())
-    full[n:] = 1234.0  # exact in fp16 and fp32
+    full[n:] = CANARY_VALUE
     return full[:n].view(*shape), full
 
 
 def canary_ok(full, n):
     tail = full[n:].float().cpu().numpy()
-    return bool(np.all(tail == 1234.0))
+    return bool(np.all(tail == CANARY_VALUE))
 
 
 def host(t):

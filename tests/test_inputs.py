@@ -65,3 +65,24 @@ def test_workload_shapes():
     assert c4["k"].dtype == np.float16 and c4["out_dtype"] == "f32"
     layers = wi.workload_inputs(3, layers=2, B=4)
     assert len(layers) == 2 and layers[0]["k"].shape == (4, 5120)
+
+
+def test_bf16_rounding_matches_round_to_nearest_even():
+    """bfloat16 inputs are fp32 values with the low 16 bits cleared by round-to-nearest-even:
+    equal to torch's fp32 -> bfloat16 conversion, exactly representable, and within half an
+    ulp of the fp32 value (8 significand bits: at most 2^-8 relative)."""
+    import torch
+    g = np.random.default_rng(5)
+    a = np.concatenate([g.standard_normal(50000) * 3, g.uniform(-1e6, 1e6, 1000), [0.0, -0.0, 1.0, 1.00390625]])
+    b = wi._round_bf16(a)
+    assert b.dtype == np.float32
+    assert np.all((b.view(np.uint32) & 0xFFFF) == 0)
+    f = a.astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(b, ref)
+    nz = f != 0
+    assert np.max(np.abs(b[nz] - f[nz]) / np.abs(f[nz])) <= 2.0 ** -8
+    assert b[-1] == 1.0  # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even
+    case = wi.forward_case(2, 8, 16, seed=3, in_dtype="bf16", gated=True)
+    for n in ("k", "v", "r"):
+        assert case[n].dtype == np.float32 and np.all((case[n].view(np.uint32) & 0xFFFF) == 0)

@@ -7,8 +7,9 @@ decay and bonus parameters.
 
 Recipe (all workloads):
   * generator: numpy PCG64 seeded with ``1000 + workload index`` unless a seed
-    is given; draws are fp64 and are rounded once (round-to-nearest-even) to
-    the I/O dtype, so both sides of every comparison consume identical values;
+    is given; draws are fp64 and are rounded (round-to-nearest-even) to the I/O
+    dtype -- once for fp32 and fp16, via fp32 for bfloat16, which is held in
+    float32 arrays -- so both sides of every comparison consume identical values;
   * decay:  time_decay_c = -5 + 8 * (c / (C-1)) ** 1.35,  w_c = -exp(time_decay_c)
   * bonus:  u_c = 0.5 * (((c + 1) mod 3) - 1) + ln(0.3)
     (the initialisation these workloads are specified with; the pages give no
@@ -66,6 +67,21 @@ WORKLOADS = {
 _NP = {"f32": np.float32, "f16": np.float16}
 
 
+def _round_bf16(a) -> np.ndarray:
+    """bfloat16 values (fp32's exponent, 8 significand bits) held in a float32 array: the
+    fp64 draw is rounded to fp32, then to bfloat16, each to nearest-even (finite inputs)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _as(a, dtype):
+    """Round an fp64 array to an I/O dtype: "f32", "f16", or "bf16" (held in float32)."""
+    if dtype == "bf16":
+        return _round_bf16(a)
+    return np.asarray(a).astype(_NP[dtype])
+
+
 def rng_for(index: int, seed: int | None = None, stream: int | None = None) -> np.random.Generator:
     """PCG64 generator: seed 1000+index by default; `stream` selects an independent
     sub-stream (used per decode layer)."""
@@ -81,7 +97,7 @@ def _normal(rng, shape, dtype, sigma=1.0, shift=0.0):
         a *= sigma
     if shift != 0.0:
         a += shift
-    return a.astype(_NP[dtype])
+    return _as(a, dtype)
 
 
 def decay_bonus(C: int):
