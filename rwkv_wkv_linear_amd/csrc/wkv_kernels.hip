@@ -488,7 +488,8 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
 // P = X v the four updates are single FMAs: num = nn + e^u P, den = dd + e^u X,
 // nn <- e^w nn + P, dd <- e^w dd + X.  The optional writes are template switches so the
 // unrolled loop has no branches: STAGE puts y in the wave's LDS v rows (each row is read
-// into registers before it is overwritten; the caller then writes 16 bytes per lane), MIX
+// into registers before it is overwritten) and writes every finished batch of rows with
+// 16-byte stores (yrow 16-byte aligned, all 64 channels in range), MIX
 // writes the time-mix xk/xv rows.  Xs holds the weights e^{k_i - kmax} from the summary
 // phase; vr, gr point at the lane's first staged row.
 template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
@@ -536,6 +537,22 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
                 yrow[i * Cu + (unsigned)lane] = yv;
             nn = fmaf(ew, nn, P);
             dd = fmaf(ew, dd, X);
+        }
+        if constexpr (STAGE) {
+            // rows h .. h+LB-1 of y are complete in LDS: write them as 16-byte chunks now, so the
+            // stores overlap the rest of the emit instead of leaving all at its end
+            __builtin_amdgcn_wave_barrier();
+            constexpr int CH16 = 16 / (int)sizeof(TOut);  // outputs per 16-byte chunk
+            constexpr int CHUNKS = CW / CH16;
+            constexpr int RPI = 64 / CHUNKS;             // rows per store instruction
+            static_assert(LB % RPI == 0, "a batch is a whole number of store instructions");
+            const int q = lane % CHUNKS, rs = lane / CHUNKS;
+#pragma unroll
+            for (int j = 0; j < LB / RPI; ++j) {
+                const int r = h + j * RPI + rs;
+                const f4 chunk = *reinterpret_cast<const f4 *>(ystage + r * CW + q * CH16);
+                *reinterpret_cast<f4 *>(yrow + r * Cu + q * CH16) = chunk;
+            }
         }
     }
     if constexpr (MODE == MODE_TIMEMIX && !MIX) xs = (float)gr[(L - 1) * CW];
@@ -775,21 +792,6 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
                 if (stage_y) RWKV_EMIT(true, false); else RWKV_EMIT(false, false);
             }
 #undef RWKV_EMIT
-            if constexpr (kStageFits) {
-                if (stage_y) {
-                    __builtin_amdgcn_wave_barrier();
-                    constexpr int CH16 = 16 / (int)sizeof(TOut);  // outputs per 16-byte chunk
-                    constexpr int CHUNKS = CW / CH16;
-                    constexpr int RPI = 64 / CHUNKS;             // rows per store instruction
-                    const int q = lane % CHUNKS, rs = lane / CHUNKS;
-#pragma unroll
-                    for (int j = 0; j < L / RPI; ++j) {
-                        const int r = j * RPI + rs;
-                        const f4 chunk = *reinterpret_cast<const f4 *>(ystage + r * CW + q * CH16);
-                        *reinterpret_cast<f4 *>(Y + row0 + (int64_t)r * C + q * CH16) = chunk;
-                    }
-                }
-            }
         } else {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
