@@ -15,7 +15,13 @@ arrays and composes the documented steps:
   * ``wkv_state``       -- the state after T tokens by its definition;
   * ``token_shift``     -- "mix current and previous token" (TR-2026-0009, Reproducibility);
   * ``timemix``         -- token shift -> WKV -> receptance gate, composed from the above;
-  * ``step``            -- one decode token: the T = 1 case of the forward.
+  * ``step``            -- one decode token: the T = 1 case of the forward;
+  * ``layer_norm``      -- LayerNorm over the channels (the "RWKV-4 14B" page, Facts table:
+                           LayerNorm before each mixer; the port report's Abstract: pre-LN);
+  * ``shift_mix``       -- the pre-LN token-shift prologue of either mixer, composed from
+                           ``layer_norm`` and ``token_shift``;
+  * ``receptance_gate`` -- channel mixing's gate and residual add (the port report's
+                           "channel-mix gating"; the 14B page's channel-mix receptance).
 
 All inputs are converted exactly to float64 (fp16/fp32 values are exact in fp64).
 """
@@ -66,6 +72,10 @@ def _load():
                                                   _dp, _dp, _dp, ctypes.c_int]
             lib.oracle_token_shift.argtypes = [_i64, _i64, _i64, _dp, _dp, _dp, _dp]
             lib.oracle_token_shift.restype = None
+            lib.oracle_layer_norm.argtypes = [_i64, _i64, _dp, _dp, _dp, ctypes.c_double, _dp]
+            lib.oracle_layer_norm.restype = None
+            lib.oracle_receptance_gate.argtypes = [_i64, _dp, _dp, _dp, _dp]
+            lib.oracle_receptance_gate.restype = None
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -222,3 +232,47 @@ def step(layer, nthreads=0):
                       nthreads=nthreads)
     st, ab = wkv_state(k, v, layer["w"], state_in=layer["state"], nthreads=nthreads)
     return dict(y=y[:, 0, :], scale=s[:, 0, :], state=st, state_abs=ab)
+
+
+def layer_norm(x, weight, bias, eps):
+    """LayerNorm of every row of x [..., C] over its channels: (x - mean) / sqrt(var + eps)
+    with the biased variance, then * weight + bias (per channel, [C])."""
+    x = _f64(x)
+    C = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    wt, bs = _f64(weight), _f64(bias)
+    out = np.empty(x.shape)
+    _load().oracle_layer_norm(rows, C, _ptr(x), _ptr(wt), _ptr(bs), float(eps), _ptr(out))
+    return out
+
+
+def shift_mix(case):
+    """Oracle outputs for an rwkv4_shift_mix case dict (see wkv_inputs.shift_mix_case): the row
+    LayerNorm when ln_weight is given (else x itself), then the token shift against x_prev (the
+    previous token's already normalised row; zeros if None) for each given mix.  Returns dict
+    with "ln" [B,T,C], "x_last" [B,C] and "xk", "xv", "xr" for the mixes present."""
+    x = _f64(case["x"])
+    B, T, C = _shape3(x)
+    if case.get("ln_weight") is not None:
+        ln = layer_norm(x, case["ln_weight"], case["ln_bias"], case["ln_eps"])
+    else:
+        ln = x
+    out = {"ln": ln}
+    xp = case.get("x_prev")
+    for name, mix in (("xk", "mix_k"), ("xv", "mix_v"), ("xr", "mix_r")):
+        if case.get(mix) is not None:
+            out[name] = token_shift(ln, xp, case[mix]) if T > 0 else np.empty((B, 0, C))
+    if T > 0:
+        out["x_last"] = ln[:, -1, :].copy()
+    else:
+        out["x_last"] = _f64(xp) if xp is not None else np.zeros((B, C))
+    return out
+
+
+def receptance_gate(r, kv, residual=None):
+    """y = residual + kv / (1 + e^{-r}) elementwise (residual None: 0)."""
+    r, kv = _f64(r), _f64(kv)
+    res = _f64(residual) if residual is not None else None
+    y = np.empty(r.shape)
+    _load().oracle_receptance_gate(r.size, _ptr(r), _ptr(kv), _ptr(res) if res is not None else None, _ptr(y))
+    return y

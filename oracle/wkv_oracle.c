@@ -309,3 +309,45 @@ void oracle_token_shift(int64_t B, int64_t T, int64_t C,
                 out[IDX(b, t, c)] = mix[c] * x[IDX(b, t, c)] + (1.0 - mix[c]) * xs;
             }
 }
+
+/*
+ * LayerNorm over the channels of every row (the "RWKV-4 14B" page, Facts table: the norm is
+ * LayerNorm and sits before each mixer, ln1 before time mixing and ln2 before channel mixing;
+ * the port report's Abstract lists pre-LN).  The textbook definition: per row, the mean and the
+ * biased variance (divided by C) of its C values, z = (x - mean) / sqrt(var + eps), and the
+ * per-channel affine out = z * weight + bias.  x and out [rows, C]; weight, bias [C].
+ */
+void oracle_layer_norm(int64_t rows, int64_t C, const double *x, const double *weight,
+                       const double *bias, double eps, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * C;
+        double mean = 0.0;
+        for (int64_t c = 0; c < C; ++c) mean += xr[c];
+        mean /= (double)C;
+        double var = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const double d = xr[c] - mean;
+            var += d * d;
+        }
+        var /= (double)C;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < C; ++c) out[r * C + c] = (xr[c] - mean) * inv * weight[c] + bias[c];
+    }
+}
+
+/*
+ * Receptance gate of channel mixing (the port report's "time-mix / channel-mix gating"; the
+ * "RWKV-4 14B" page, field table: channel mixing has its own d x d receptance matrix):
+ * y = residual + kv / (1 + e^{-r}) elementwise over n values; residual NULL = 0.
+ */
+void oracle_receptance_gate(int64_t n, const double *r, const double *kv, const double *residual,
+                            double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const double g = kv[i] / (1.0 + exp(-r[i]));
+        y[i] = residual ? residual[i] + g : g;
+    }
+}

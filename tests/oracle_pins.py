@@ -10,7 +10,10 @@ Each function raises AssertionError when the oracle disagrees with:
   * invariants (constant v, affine equivariance, convexity, shift invariance,
     state carried across a split sequence, canonical state with bb >= 1);
   * the two independent forms inside the oracle (direct sums vs recurrence)
-    and a 50-digit mpmath evaluation of the sums (rounding only).
+    and a 50-digit mpmath evaluation of the sums (rounding only);
+  * for the pre-LN prologue and the channel-mix gate: hand-worked examples
+    (tests/golden/layer_norm_shift_gate_hand_worked.json), LayerNorm's closed-form
+    moments and invariances, torch's float64 layer_norm, and scipy's expit.
 
 They are plain functions so that the mutation tests can run them against
 deliberately wrong builds of the oracle.
@@ -341,10 +344,85 @@ def pin_mpmath_precision():
                 assert abs(float(yv - mpf(got))) <= 1e-13 * sd[0, t, c], "mpmath precision"
 
 
+# ----------------------------------------------------------------------------- pre-LN prologue and gate
+
+def _golden_mix():
+    with open(os.path.join(GOLDEN, "layer_norm_shift_gate_hand_worked.json")) as f:
+        return json.load(f)
+
+
+def pin_layer_norm_hand_worked():
+    g = _golden_mix()["layer_norm"]
+    for case in g["cases"]:
+        out = oracle.layer_norm(np.array([case["x"]], dtype=np.float64), g["weight"], g["bias"], case["eps"])
+        _close(out[0], case["out"], 1e-14, f"layer norm of {case['x']} (eps {case['eps']})")
+
+
+def pin_layer_norm_moments():
+    # eps = 0, unit weight, zero bias: every row has mean 0 and mean square 1 exactly
+    g = _rng(21)
+    x = g.normal(0, 1, (7, 53)) * g.uniform(0.1, 30, (7, 1)) + g.normal(0, 50, (7, 1))
+    z = oracle.layer_norm(x, np.ones(53), np.zeros(53), 0.0)
+    assert np.max(np.abs(z.mean(axis=1))) <= 1e-13, "layer norm: row mean not 0"
+    assert np.max(np.abs((z * z).mean(axis=1) - 1.0)) <= 1e-13, "layer norm: row mean square not 1"
+
+
+def pin_layer_norm_library():
+    import torch
+    g = _rng(22)
+    x = g.normal(0, 1, (3, 5, 37)) * 2.5 + 0.7
+    wt, bs = g.normal(1, 0.3, 37), g.normal(0, 0.2, 37)
+    for eps in (1e-5, 0.5):
+        want = torch.nn.functional.layer_norm(torch.from_numpy(x), (37,), torch.from_numpy(wt),
+                                              torch.from_numpy(bs), eps).numpy()
+        _close(oracle.layer_norm(x, wt, bs, eps), want, 1e-12, f"layer norm vs torch (eps {eps})")
+
+
+def pin_layer_norm_invariance():
+    # with eps = 0 a row's affine change a*x + b (a > 0) cancels; a sign flip flips z
+    g = _rng(23)
+    x = g.normal(0, 1, (4, 29))
+    wt, bs = g.normal(1, 0.3, 29), g.normal(0, 0.2, 29)
+    base = oracle.layer_norm(x, wt, bs, 0.0)
+    _close(oracle.layer_norm(3.7 * x - 11.0, wt, bs, 0.0), base, 1e-12, "layer norm: affine invariance")
+    z = oracle.layer_norm(x, np.ones(29), np.zeros(29), 0.0)
+    _close(oracle.layer_norm(-x, np.ones(29), np.zeros(29), 0.0), -z, 1e-13, "layer norm: odd symmetry")
+
+
+def pin_shift_mix_hand_worked():
+    g = _golden_mix()["shift_mix"]
+    x = np.array([g["x"]], dtype=np.float64)
+    case = dict(x=x, x_prev=np.array([g["x_prev"]], dtype=np.float64), ln_weight=np.array(g["weight"], float),
+                ln_bias=np.array(g["bias"], float), ln_eps=g["eps"], mix_k=np.array(g["mix"], float),
+                mix_v=None, mix_r=np.array(g["mix"], float))
+    out = oracle.shift_mix(case)
+    _close(out["xk"][0], g["out"], 1e-15, "shift-mix hand-worked")
+    _close(out["xr"][0], g["out"], 1e-15, "shift-mix hand-worked (xr)")
+    _close(out["x_last"][0], g["x_last"], 1e-15, "shift-mix x_last")
+    assert "xv" not in out, "shift-mix produced an output with no mix"
+    # without LayerNorm the prologue is the bare token shift
+    case.update(ln_weight=None, ln_bias=None)
+    xs = np.concatenate([case["x_prev"][:, None, :], x[:, :-1, :]], axis=1)
+    mix = case["mix_k"]
+    _close(oracle.shift_mix(case)["xk"], mix * x + (1 - mix) * xs, 1e-15, "shift-mix without LayerNorm")
+
+
+def pin_receptance_gate():
+    g = _golden_mix()["gate"]
+    r = np.array([_parse(e) for e in g["r"]])
+    _close(oracle.receptance_gate(r, g["kv"], g["residual"]), g["y"], 1e-15, "gate hand-worked")
+    rng = _rng(24)
+    r, kv, res = rng.normal(0, 3, 101), rng.normal(0, 1, 101), rng.normal(0, 1, 101)
+    _close(oracle.receptance_gate(r, kv, res), res + expit(r) * kv, 1e-14, "gate = residual + expit(r) kv")
+    _close(oracle.receptance_gate(r, kv), expit(r) * kv, 1e-14, "gate without residual")
+
+
 ALL_PINS = [
     pin_hand_worked, pin_full_forgetting, pin_impulse_geometric, pin_prior_geometric,
     pin_cumulative_mean, pin_softmax_mean, pin_gate_logistic, pin_token_shift_library,
     pin_constant_v, pin_affine_equivariance, pin_convexity_and_scale, pin_shift_invariance,
     pin_state_split_carry, pin_state_canonical, pin_direct_vs_recurrence,
-    pin_points_match_direct, pin_mpmath_precision,
+    pin_points_match_direct, pin_mpmath_precision, pin_layer_norm_hand_worked,
+    pin_layer_norm_moments, pin_layer_norm_library, pin_layer_norm_invariance,
+    pin_shift_mix_hand_worked, pin_receptance_gate,
 ]

@@ -41,6 +41,15 @@ MUTANTS = [
      "(double)(age + 1) * wc + k[IDX(b, i, c)]", True),
     ("scale uses signed v", "absn += e * fabs(vl[i * stride]);", "absn += e * vl[i * stride];", False),
     ("recurrence scale uses signed v", "A = ew * A + ek * fabs(vt);", "A = ew * A + ek * vt;", False),
+    ("layer norm: unbiased variance", "var /= (double)C;", "var /= (double)(C - 1);", False),
+    ("layer norm: mean over one value too many", "mean /= (double)C;", "mean /= (double)(C + 1);", False),
+    ("layer norm: eps outside the root", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)", False),
+    ("layer norm: mean not subtracted", "out[r * C + c] = (xr[c] - mean) * inv", "out[r * C + c] = xr[c] * inv",
+     False),
+    ("layer norm: weight and bias swapped", "* inv * weight[c] + bias[c]", "* inv * bias[c] + weight[c]", False),
+    ("gate: sign flipped", "kv[i] / (1.0 + exp(-r[i]))", "kv[i] / (1.0 + exp(r[i]))", False),
+    ("gate: receptance and value swapped", "kv[i] / (1.0 + exp(-r[i]))", "r[i] / (1.0 + exp(-kv[i]))", False),
+    ("gate: residual dropped", "y[i] = residual ? residual[i] + g : g;", "y[i] = g;", False),
 ]
 
 

@@ -20,6 +20,12 @@ Recipe (all workloads):
 The five named workloads follow the shapes of the RWKV-4 169m and 14B models
 (d_model 768 and 5120, 40 layers, 1K context) and a long-context case at
 hidden size 2048 (the RWKV-GLM card's width).
+
+The mixers' elementwise prologue and epilogue (pre-LN token shift, channel-mix receptance
+gate) draw their own cases: activations N(0,1) with, for the LayerNorm input, a per-row
+offset N(0, 2^2) and scale U(0.5, 4) so the row statistics matter; LayerNorm weight
+N(1, 0.25^2) and bias N(0, 0.1^2) in fp32 (the pages give no trained values); eps 1e-5;
+mixes U(0,1); the gate's receptance N(0, 2^2).
 """
 from __future__ import annotations
 
@@ -30,8 +36,13 @@ import numpy as np
 
 __all__ = [
     "WORKLOADS", "Workload", "decay_bonus", "forward_case", "timemix_case",
-    "step_layer", "prior_state", "workload_inputs", "rng_for",
+    "step_layer", "prior_state", "workload_inputs", "rng_for", "shift_mix_case", "gate_case",
+    "LN_EPS",
 ]
+
+# LayerNorm epsilon of the prologue cases: the pages give none; 1e-5 is the usual default of
+# a LayerNorm layer.
+LN_EPS = 1e-5
 
 
 @dataclass(frozen=True)
@@ -179,3 +190,38 @@ def workload_inputs(index: int, seed: int | None = None, **shape):
         return [step_layer(l, B, C, seed=s, in_dtype=wl.in_dtype, index=index)
                 for l in range(layers)]
     raise ValueError(wl.kind)
+
+
+def shift_mix_case(B, T, C, *, seed, dtype="f16", ln=True, mixes="kvr", prior=True,
+                   row_stats=True, index=5):
+    """Inputs for rwkv4_shift_mix.  Draw order: x, [row offsets, row scales], x_prev,
+    [ln_weight, ln_bias], mix_k, mix_v, mix_r (each mix drawn whether or not it is used, so a
+    case's values do not depend on which outputs are requested)."""
+    g = rng_for(index, seed)
+    a = g.standard_normal((B, T, C))
+    if row_stats:
+        off = g.normal(0.0, 2.0, (B, T, 1))
+        sc = g.uniform(0.5, 4.0, (B, T, 1))
+        a = a * sc + off
+    x = _as(a, dtype)
+    x_prev = _normal(g, (B, C), dtype) if prior else None
+    if ln:
+        ln_w = g.normal(1.0, 0.25, C).astype(np.float32)
+        ln_b = g.normal(0.0, 0.1, C).astype(np.float32)
+    else:
+        ln_w = ln_b = None
+    mk = g.uniform(0.0, 1.0, C).astype(np.float32)
+    mv = g.uniform(0.0, 1.0, C).astype(np.float32)
+    mr = g.uniform(0.0, 1.0, C).astype(np.float32)
+    return dict(B=B, T=T, C=C, x=x, x_prev=x_prev, ln_weight=ln_w, ln_bias=ln_b, ln_eps=LN_EPS,
+                mix_k=mk if "k" in mixes else None, mix_v=mv if "v" in mixes else None,
+                mix_r=mr if "r" in mixes else None, dtype=dtype)
+
+
+def gate_case(n, *, seed, in_dtype="f16", out_dtype=None, residual=True, index=6):
+    """Inputs for rwkv4_channelmix_gate over n elements.  Draw order: r, kv, [residual]."""
+    g = rng_for(index, seed)
+    r = _normal(g, (n,), in_dtype, sigma=2.0)
+    kv = _normal(g, (n,), in_dtype)
+    res = _normal(g, (n,), in_dtype) if residual else None
+    return dict(n=n, r=r, kv=kv, residual=res, in_dtype=in_dtype, out_dtype=out_dtype or in_dtype)
