@@ -19,6 +19,8 @@ K back-to-back launches), and the fp64 CPU oracle timed on the host cores.
   gated169m  rwkv4_wkv_forward  B8 T1024 C768, fp16 in/out, gated, prior state
   decode14b  40 x rwkv4_wkv_step  B256 C5120, fp16, gated, state in place (a step = 40 layers)
   long       rwkv4_wkv_forward  B1 T65536 C2048, fp16 in, fp32 out
+  lnshift14b rwkv4_shift_mix    B1 T1024 C5120 fp16: LayerNorm + token shift -> xk, xv, xr, x_last
+  cmgate14b  rwkv4_channelmix_gate  1024 x 5120 fp16: residual + sigmoid(r) * kv
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--chunk-len L] [--algo A]
     python bench.py --copy-kernel      # plain device copy, for counter calibration
@@ -50,6 +52,8 @@ WORKLOADS = {
     "gated169m": (1, "rwkv4-169m gated prefill B8 T1024 C768 (fp16 I/O, prior state)"),
     "decode14b": (3, "rwkv4-14b batched decode, 40 layers x B256 C5120 (fp16 I/O, state in place)"),
     "long": (4, "long-sequence forward B1 T65536 C2048 (fp16 in, fp32 out)"),
+    "lnshift14b": (5, "rwkv4-14b time-mix prologue: ln1 + token shift -> xk, xv, xr, B1 T1024 C5120 (fp16)"),
+    "cmgate14b": (6, "rwkv4-14b channel-mix gate + residual, B1 T1024 C5120 (fp16)"),
 }
 CPU_BUDGET_S = 10.0  # CPU seconds the oracle leg spends (at least 3 runs)
 
@@ -106,7 +110,9 @@ def cpu_baseline(name, case, elements, sample):
     """The fp64 oracle as it stands, on the host cores: median of repeated runs over
     `case` (at least 3, about CPU_BUDGET_S seconds in all)."""
     import oracle
-    run = {"timemix14b": oracle.timemix, "decode14b": lambda c: [oracle.step(l) for l in c]}.get(
+    run = {"timemix14b": oracle.timemix, "decode14b": lambda c: [oracle.step(l) for l in c],
+           "lnshift14b": oracle.shift_mix,
+           "cmgate14b": lambda c: oracle.receptance_gate(c["r"], c["kv"], c["residual"])}.get(
         name, oracle.forward)
     times = []
     t_end = time.perf_counter() + CPU_BUDGET_S
@@ -201,6 +207,9 @@ class Setup:
         E = B * T * C
         self.elements = E
         self.launches_per_step = 1
+        if wl.kind in ("shift", "gate"):
+            self._setup_mix(wl, case, args, torch, rw, np, dev, hs, E)
+            return
         if wl.kind == "timemix":
             self.entry = "rwkv4_timemix_fused"
             self.fn = rw.lib.rwkv4_timemix_fused
@@ -257,6 +266,54 @@ class Setup:
         self.cpu_elements = E
         self.cpu_sample = f"the full workload B{B} T{T} C{C}"
 
+    def _setup_mix(self, wl, case, args, torch, rw, np, dev, hs, E):
+        """Buffers of the prologue (LayerNorm + token shift) and gate workloads."""
+        B, T, C = self.B, self.T, self.C
+        vp = ctypes.c_void_p
+        f16 = torch.float16
+
+        def dev_t(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        if wl.kind == "shift":
+            self.entry = "rwkv4_shift_mix"
+            self.fn = rw.lib.rwkv4_shift_mix
+            # x read, xk, xv, xr written (2 B each), x_prev read and x_last written, LayerNorm
+            # weight and bias and three mixes (fp32 per channel)
+            self.launch_bytes = 4 * 2 * E + 2 * 2 * B * C + 5 * 4 * C
+            hx = torch.from_numpy(np.ascontiguousarray(case["x"]))
+            sh = {n: dev_t(case[n]) for n in ("x_prev", "ln_weight", "ln_bias", "mix_k", "mix_v", "mix_r")}
+            self.keep.append(sh)
+            R = max(2, math.ceil(args.rotate_gib * 2**30 / (8 * E)))
+            self.sets = []
+            for _ in range(R):
+                s = dict(x=hx.to(dev), **{n: torch.empty((B, T, C), dtype=f16, device=dev) for n in ("xk", "xv", "xr")},
+                         x_last=torch.empty((B, C), dtype=f16, device=dev))
+                self.keep.append(s)
+                self.sets.append([(B, T, C, vp(s["x"].data_ptr()), vp(sh["x_prev"].data_ptr()),
+                                   vp(s["x_last"].data_ptr()), vp(sh["ln_weight"].data_ptr()),
+                                   vp(sh["ln_bias"].data_ptr()), ctypes.c_float(case["ln_eps"]),
+                                   vp(sh["mix_k"].data_ptr()), vp(sh["mix_v"].data_ptr()),
+                                   vp(sh["mix_r"].data_ptr()), vp(s["xk"].data_ptr()), vp(s["xv"].data_ptr()),
+                                   vp(s["xr"].data_ptr()), rw.RWKV_F16, hs)])
+        else:
+            self.entry = "rwkv4_channelmix_gate"
+            self.fn = rw.lib.rwkv4_channelmix_gate
+            # r, kv, residual read and y written, 2 B each
+            self.launch_bytes = 4 * 2 * E
+            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in ("r", "kv", "residual")}
+            R = max(2, math.ceil(args.rotate_gib * 2**30 / (8 * E)))
+            self.sets = []
+            for _ in range(R):
+                s = {n: h[n].to(dev) for n in h}
+                s["y"] = torch.empty(E, dtype=f16, device=dev)
+                self.keep.append(s)
+                self.sets.append([(E, vp(s["r"].data_ptr()), vp(s["kv"].data_ptr()), vp(s["residual"].data_ptr()),
+                                   vp(s["y"].data_ptr()), rw.RWKV_F16, rw.RWKV_F16, hs)])
+        self.cpu_case = case
+        self.cpu_elements = E
+        self.cpu_sample = f"the full workload B{B} T{T} C{C}"
+
     def step(self, i, rw):
         for call in self.sets[i % len(self.sets)]:
             st = self.fn(*call)
@@ -279,7 +336,8 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     name = args.workload
     su = Setup(name, args, torch, rw, wi, np)
-    default_steps = {"timemix14b": 1000, "plain169m": 1000, "gated169m": 500, "decode14b": 100, "long": 50}
+    default_steps = {"timemix14b": 1000, "plain169m": 1000, "gated169m": 500, "decode14b": 100, "long": 50,
+                     "lnshift14b": 1000, "cmgate14b": 1000}
     K = args.steps if args.steps is not None else default_steps[name]
     W = args.warmup if args.warmup is not None else max(5, K // 20)
 

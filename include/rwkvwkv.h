@@ -162,6 +162,43 @@ rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C,
                                 const float *state_in, float *state_out,
                                 hipStream_t stream, const rwkv4_opts *opts);
 
+/*
+ * Pre-LN token-shift prologue of either mixer (the "RWKV-4 14B" page, Facts table: a LayerNorm
+ * before each mixer, ln1 before time mixing and ln2 before channel mixing; the port report's
+ * Abstract: pre-LN and the token shift that mixes the current and previous token).  Per batch
+ * row and token t, over the C channels of the row:
+ *   n_t = (x_t - mean_t) / sqrt(var_t + ln_eps) * ln_weight + ln_bias
+ *         (mean and biased variance of the row; n_t = x_t when ln_weight is NULL),
+ *   xk_t = mix_k * n_t + (1 - mix_k) * n_{t-1}, and xv, xr likewise (fp32 math, one rounding),
+ *   with n_{-1} = x_prev (the previous token's row, already normalised: a previous call's
+ *   x_last; zeros when NULL), and x_last = n_{T-1} (x_prev, or zeros, when T = 0).
+ * Time mixing asks for xk, xv, xr; channel mixing for xk, xr.
+ *   x, xk, xv, xr [B,T,C] and x_prev, x_last [B,C] use dtype; ln_weight, ln_bias and the
+ *   mixes are fp32 [C].  ln_bias may be NULL (zero) when ln_weight is set and must be NULL
+ *   when it is not; ln_eps >= 0 and finite.  Each of xk, xv, xr is written exactly when its
+ *   mix is given (both or neither when T > 0, else RWKV_ERR_ARG).  x_last may equal x_prev (the shift
+ *   state updated in place); no other output may overlap an input or another output.
+ */
+rwkv_status rwkv4_shift_mix(int64_t B, int64_t T, int64_t C,
+                            const void *x, const void *x_prev, void *x_last,
+                            const float *ln_weight, const float *ln_bias, float ln_eps,
+                            const float *mix_k, const float *mix_v, const float *mix_r,
+                            void *xk, void *xv, void *xr,
+                            rwkv_dtype dtype, hipStream_t stream);
+
+/*
+ * Receptance gate of channel mixing with the residual add (the port report's "channel-mix
+ * gating"; the "RWKV-4 14B" page's field table: channel mixing has its own d x d receptance
+ * matrix; the page's pre-norm placement puts the block's output on the residual stream):
+ *   y = residual + kv / (1 + e^{-r})   elementwise over n values (residual NULL: 0),
+ * where r and kv are the caller's projections (receptance, and value of the activated key).
+ *   r, kv, residual: n values of in_dtype; y: n values of out_dtype.  y may be residual itself
+ *   when the dtypes are equal (an in-place residual add); no other overlap.  n = 0 is a no-op.
+ */
+rwkv_status rwkv4_channelmix_gate(int64_t n, const void *r, const void *kv, const void *residual,
+                                  void *y, rwkv_dtype in_dtype, rwkv_dtype out_dtype,
+                                  hipStream_t stream);
+
 /* Static text for a status code. */
 const char *rwkv_status_string(rwkv_status s);
 

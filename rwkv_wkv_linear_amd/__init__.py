@@ -64,6 +64,11 @@ def _load():
     lib.rwkv4_timemix_fused.argtypes = [i64, i64, i64, vp, vp, vp, fp, fp, fp, vp, vp, fp, fp, vp, vp, vp,
                                         fp, fp, vp, ctypes.POINTER(Opts)]
     lib.rwkv4_timemix_fused.restype = ctypes.c_int
+    lib.rwkv4_shift_mix.argtypes = [i64, i64, i64, vp, vp, vp, fp, fp, ctypes.c_float, fp, fp, fp, vp, vp, vp,
+                                    ctypes.c_int, vp]
+    lib.rwkv4_shift_mix.restype = ctypes.c_int
+    lib.rwkv4_channelmix_gate.argtypes = [i64, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.rwkv4_channelmix_gate.restype = ctypes.c_int
     lib.rwkv_status_string.argtypes = [ctypes.c_int]
     lib.rwkv_status_string.restype = ctypes.c_char_p
     lib.rwkv_last_error.argtypes = []
@@ -270,8 +275,58 @@ def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, x
     return y
 
 
+def rwkv4_shift_mix(x, x_prev=None, *, ln_weight=None, ln_bias=None, ln_eps=1e-5, mix_k=None, mix_v=None,
+                    mix_r=None, xk=None, xv=None, xr=None, x_last=None, stream=None):
+    """Pre-LN token-shift prologue: n = LayerNorm(x) over the channels (x itself when ln_weight
+    is None); for each given mix, out = mix * n_t + (1 - mix) * n_{t-1} with n_{-1} = x_prev.
+    x [B, T, C]; x_prev, x_last [B, C] (x's dtype; x_last may be x_prev itself); ln_*, mix_* [C]
+    float32.  Outputs not passed are allocated for each given mix.  Returns (xk, xv, xr, x_last)
+    (None where not requested)."""
+    torch = _torch()
+    B, T, C = x.shape
+    dev, dt = x.device, x.dtype
+    _need(x, "x", dtype=dt)
+    _need(x_prev, "x_prev", (B, C), dt, dev)
+    _need(x_last, "x_last", (B, C), dt, dev)
+    for name, m in (("ln_weight", ln_weight), ("ln_bias", ln_bias), ("mix_k", mix_k), ("mix_v", mix_v),
+                    ("mix_r", mix_r)):
+        _need(m, name, (C,), torch.float32, dev)
+    outs = []
+    for name, mix, o in (("xk", mix_k, xk), ("xv", mix_v, xv), ("xr", mix_r, xr)):
+        if mix is not None and o is None:
+            o = torch.empty((B, T, C), dtype=dt, device=dev)
+        _need(o, name, (B, T, C), dt, dev)
+        outs.append(o)
+    with torch.cuda.device(dev):
+        _check(_get_lib().rwkv4_shift_mix(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(ln_weight),
+                                          _ptr(ln_bias), float(ln_eps), _ptr(mix_k), _ptr(mix_v), _ptr(mix_r),
+                                          _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _dtype_code(dt),
+                                          _stream(stream, dev)))
+    return outs[0], outs[1], outs[2], x_last
+
+
+def rwkv4_channelmix_gate(r, kv, residual=None, y=None, *, out_dtype=None, stream=None):
+    """y = residual + kv / (1 + e^{-r}) elementwise (residual None: 0).  r, kv, residual share a
+    shape and dtype; y (allocated if None) has that shape and out_dtype (default r's dtype) and
+    may be residual itself."""
+    torch = _torch()
+    dev, dt = r.device, r.dtype
+    _need(r, "r", dtype=dt)
+    _need(kv, "kv", tuple(r.shape), dt, dev)
+    _need(residual, "residual", tuple(r.shape), dt, dev)
+    odt = out_dtype or (y.dtype if y is not None else dt)
+    if y is None:
+        y = torch.empty(r.shape, dtype=odt, device=dev)
+    _need(y, "y", tuple(r.shape), odt, dev)
+    with torch.cuda.device(dev):
+        _check(_get_lib().rwkv4_channelmix_gate(r.numel(), _ptr(r), _ptr(kv), _ptr(residual), _ptr(y),
+                                                _dtype_code(dt), _dtype_code(odt), _stream(stream, dev)))
+    return y
+
+
 __all__ = [
     "lib", "LIB_PATH", "Opts", "RwkvError", "header_functions", "status_string",
     "rwkv4_wkv_forward", "rwkv4_wkv_step", "rwkv4_timemix_fused", "rwkv_status_string",
-    "rwkv_last_error", "rwkv4_workspace_bytes", "rwkv_abi_version",
+    "rwkv_last_error", "rwkv4_workspace_bytes", "rwkv_abi_version", "rwkv4_shift_mix",
+    "rwkv4_channelmix_gate",
 ]

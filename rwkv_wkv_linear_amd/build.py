@@ -14,10 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librwkvwkv.so")
-SOURCES = ["wkv_kernels.hip", "rwkvwkv_abi.hip"]
+SOURCES = ["wkv_kernels.hip", "mix_kernels.hip", "rwkvwkv_abi.hip"]
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     "--offload-arch=gfx950",
     # no packed FP32 instructions anywhere (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,21 +30,43 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []),
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _run(cmds, verbose):
+    """Run the commands in parallel; raise with their diagnostics if any fails."""
     # hipcc's host pass does not know the packed-fp32 feature name; drop that warning only
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    errlines = [l for l in res.stderr.splitlines() if noise not in l]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(errlines))
-    if verbose and errlines:
-        print("\n".join(errlines), file=sys.stderr)
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = []
+    for cmd, p in zip(cmds, procs):
+        _, err = p.communicate()
+        errlines = [l for l in err.splitlines() if noise not in l]
+        if p.returncode != 0:
+            failed.append(" ".join(cmd[-3:]) + "\n" + "\n".join(errlines))
+        elif verbose and errlines:
+            print("\n".join(errlines), file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n\n".join(failed))
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source to an object in parallel, then link the shared library."""
+    tag = "%d" % os.getpid()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".%s.o" % tag) for s in SOURCES]
+    _run([[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *inc, "-c", os.path.join(CSRC, s), "-o", o]
+          for s, o in zip(SOURCES, objs)], verbose)
+    tmp = LIB + ".tmp" + tag
+    try:
+        _run([[hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]], verbose)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     os.replace(tmp, LIB)
     return LIB
 

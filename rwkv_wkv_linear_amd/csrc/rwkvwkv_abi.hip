@@ -320,6 +320,103 @@ rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C, const void *x, 
     return run_forward(a, o, stream);
 }
 
+rwkv_status rwkv4_shift_mix(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,
+                            void *x_last, const float *ln_weight, const float *ln_bias, float ln_eps,
+                            const float *mix_k, const float *mix_v, const float *mix_r, void *xk,
+                            void *xv, void *xr, rwkv_dtype dtype, hipStream_t stream) {
+    rwkv_status s;
+    if ((s = check_dtype(dtype, "dtype")) != RWKV_OK) return s;
+    if (B < 1 || C < 1 || T < 0)
+        return fail(RWKV_ERR_ARG, "sizes must satisfy B >= 1, C >= 1, T >= 0 (got %lld, %lld, %lld)",
+                    (long long)B, (long long)T, (long long)C);
+    if (B > kMaxElems / C || (T > 0 && B * C > kMaxElems / T)) return fail(RWKV_ERR_ARG, "B*T*C too large");
+    if (B * ((T + 2) / 3 + 1) > 0x7fffffffLL) return fail(RWKV_ERR_ARG, "B*T too large for one launch");
+    if (T > 0 && !x) return fail(RWKV_ERR_ARG, "x is required when T > 0");
+    if (!ln_weight && ln_bias) return fail(RWKV_ERR_ARG, "ln_bias is set but ln_weight is not");
+    if (ln_weight && !(ln_eps >= 0.f && ln_eps <= 3.0e38f))
+        return fail(RWKV_ERR_ARG, "ln_eps must be finite and >= 0");
+    const float *mix[3] = {mix_k, mix_v, mix_r};
+    void *out[3] = {xk, xv, xr};
+    const char *names[3] = {"xk", "xv", "xr"};
+    for (int i = 0; i < 3; ++i)  // with no tokens there is nothing to write (outputs may be NULL)
+        if (T > 0 && (mix[i] == nullptr) != (out[i] == nullptr))
+            return fail(RWKV_ERR_ARG, "%s and its mix must be given together", names[i]);
+    const size_t e = esize(dtype);
+    for (const void *p : {x, x_prev, (const void *)x_last, (const void *)xk, (const void *)xv, (const void *)xr})
+        if (p && !aligned(p, e)) return fail(RWKV_ERR_ALIGN, "activation pointer %p not aligned to %zu bytes", p, e);
+    for (const float *p : {ln_weight, ln_bias, mix_k, mix_v, mix_r})
+        if (p && !aligned(p, 4)) return fail(RWKV_ERR_ALIGN, "fp32 pointer %p not 4-byte aligned", (const void *)p);
+    const size_t act = (size_t)(B * T * C) * e, row = (size_t)(B * C) * e;
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(out[i], act, x, act) || overlap(out[i], act, x_prev, row) || overlap(out[i], act, x_last, row))
+            return fail(RWKV_ERR_ARG, "%s overlaps x, x_prev or x_last", names[i]);
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], act, out[j], act)) return fail(RWKV_ERR_ARG, "%s overlaps %s", names[i], names[j]);
+    }
+    if (overlap(x_last, row, x, act)) return fail(RWKV_ERR_ARG, "x_last overlaps x");
+    if (x_last && x_prev && x_last != x_prev && overlap(x_last, row, x_prev, row))
+        return fail(RWKV_ERR_ARG, "x_last overlaps x_prev without being equal to it");
+    ShiftMixArgs a{};
+    a.B = B;
+    a.T = T;
+    a.C = C;
+    a.x = x;
+    a.x_prev = x_prev;
+    a.x_last = x_last;
+    a.ln_weight = ln_weight;
+    a.ln_bias = ln_bias;
+    a.ln_eps = ln_eps;
+    bool vec = (C % 8) == 0;
+    for (int i = 0; i < 3; ++i) {
+        a.mix[i] = T > 0 ? mix[i] : nullptr;
+        a.out[i] = T > 0 ? out[i] : nullptr;
+        if ((mix[i] && !aligned(mix[i], 16)) || (out[i] && !aligned(out[i], 16))) vec = false;
+    }
+    for (const void *p : {x, x_prev, (const void *)x_last, (const void *)ln_weight, (const void *)ln_bias})
+        if (p && !aligned(p, 16)) vec = false;
+    a.vec = vec ? 1 : 0;
+    a.dt = dtype;
+    if (T == 0 && !x_last) return ok();
+    const hipError_t err = launch_shift_mix(a, stream);
+    if (err != hipSuccess) return hip_fail(err, "launch (shift-mix)");
+    return ok();
+}
+
+rwkv_status rwkv4_channelmix_gate(int64_t n, const void *r, const void *kv, const void *residual, void *y,
+                                  rwkv_dtype in_dtype, rwkv_dtype out_dtype, hipStream_t stream) {
+    rwkv_status s;
+    if ((s = check_dtype(in_dtype, "in_dtype")) != RWKV_OK) return s;
+    if ((s = check_dtype(out_dtype, "out_dtype")) != RWKV_OK) return s;
+    if (n < 0 || n > kMaxElems) return fail(RWKV_ERR_ARG, "n must be in [0, 2^46] (got %lld)", (long long)n);
+    if (n == 0) return ok();
+    if (!r || !kv || !y) return fail(RWKV_ERR_ARG, "r, kv and y are required");
+    const size_t ei = esize(in_dtype), eo = esize(out_dtype);
+    for (const void *p : {r, kv, residual})
+        if (p && !aligned(p, ei)) return fail(RWKV_ERR_ALIGN, "input pointer %p not aligned to %zu bytes", p, ei);
+    if (!aligned(y, eo)) return fail(RWKV_ERR_ALIGN, "y not aligned to %zu bytes", eo);
+    const size_t bi = (size_t)n * ei, bo = (size_t)n * eo;
+    // y may be the residual itself (an in-place residual add: each element is read before it
+    // is written by the same thread); no other overlap
+    if (overlap(y, bo, r, bi) || overlap(y, bo, kv, bi) ||
+        (residual && (y != residual || eo != ei) && overlap(y, bo, residual, bi)))
+        return fail(RWKV_ERR_ARG, "y overlaps an input (only y == residual with equal dtypes is allowed)");
+    GateLaunch g{};
+    g.n = n;
+    g.r = r;
+    g.kv = kv;
+    g.residual = residual;
+    g.y = y;
+    g.in_dt = in_dtype;
+    g.out_dt = out_dtype;
+    bool vec = (n % 8) == 0;
+    for (const void *p : {r, kv, residual, (const void *)y})
+        if (p && !aligned(p, 16)) vec = false;
+    g.vec = vec ? 1 : 0;
+    const hipError_t err = launch_gate(g, stream);
+    if (err != hipSuccess) return hip_fail(err, "launch (channel-mix gate)");
+    return ok();
+}
+
 const char *rwkv_status_string(rwkv_status s) {
     switch (s) {
         case RWKV_OK: return "ok";

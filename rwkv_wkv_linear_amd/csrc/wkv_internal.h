@@ -72,4 +72,28 @@ constexpr int kTwoPassMaxTiles = 0;
 // T == 0: state_out <- state_in (or the empty state), x_last <- x_prev (or zeros).
 hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s);
 
+// Pre-LN token-shift prologue (mix_kernels.hip).
+struct ShiftMixArgs {
+    int64_t B, T, C;
+    const void *x, *x_prev;
+    void *x_last;
+    const float *ln_weight, *ln_bias;  // ln_weight null: no LayerNorm
+    float ln_eps;
+    const float *mix[3];  // k, v, r; each may be null
+    void *out[3];         // xk, xv, xr; null exactly when its mix is
+    int dt;               // rwkv_dtype code of x, x_prev, x_last and the outputs
+    int vec;              // 1: C % 8 == 0 and every pointer 16-byte aligned
+};
+hipError_t launch_shift_mix(const ShiftMixArgs &a, hipStream_t s);
+
+// Channel-mix receptance gate (mix_kernels.hip): y = residual + kv / (1 + e^{-r}).
+struct GateLaunch {
+    int64_t n;
+    const void *r, *kv, *residual;  // residual may be null
+    void *y;
+    int in_dt, out_dt;
+    int vec;  // 1: n % 8 == 0 and every pointer 16-byte aligned
+};
+hipError_t launch_gate(const GateLaunch &g, hipStream_t s);
+
 }  // namespace rwkvwkv

@@ -163,3 +163,48 @@ def test_workspace_bytes():
     # two-pass aggregates (tiles * 64 channels * 4 fp32)
     tiles = 32 * 1024
     assert a == tiles * 4 * 64 * 8 + 256 + tiles * 64 * 16
+
+
+def shift(B=2, T=8, C=16, x=p(0x100000), x_prev=None, x_last=None, ln_w=p(0x10000), ln_b=p(0x20000),
+          eps=1e-5, mk=p(0x30000), mv=None, mr=p(0x50000), xk=p(0x400000), xv=None, xr=p(0x600000), dt=1):
+    return L.rwkv4_shift_mix(B, T, C, x, x_prev, x_last, ln_w, ln_b, eps, mk, mv, mr, xk, xv, xr, dt, None)
+
+
+def test_shift_mix_validation():
+    assert shift(B=0) == rw.RWKV_ERR_ARG and "sizes" in rw.rwkv_last_error()
+    assert shift(T=-1) == rw.RWKV_ERR_ARG
+    assert shift(dt=5) == rw.RWKV_ERR_DTYPE
+    assert shift(x=None) == rw.RWKV_ERR_ARG                          # x required when T > 0
+    assert shift(ln_w=None) == rw.RWKV_ERR_ARG                       # bias without weight
+    assert shift(eps=-1.0) == rw.RWKV_ERR_ARG and "ln_eps" in rw.rwkv_last_error()
+    assert shift(eps=float("inf")) == rw.RWKV_ERR_ARG
+    assert shift(eps=float("nan")) == rw.RWKV_ERR_ARG
+    assert shift(xk=None) == rw.RWKV_ERR_ARG                         # a mix without its output
+    assert shift(xv=p(0x500000)) == rw.RWKV_ERR_ARG                  # an output without its mix
+    assert shift(x=p(0x100001)) == rw.RWKV_ERR_ALIGN                 # fp16 needs 2-byte alignment
+    assert shift(mk=p(0x30002)) == rw.RWKV_ERR_ALIGN
+    assert shift(dt=0, xr=p(0x600002)) == rw.RWKV_ERR_ALIGN          # fp32 needs 4 bytes
+    assert shift(xk=p(0x100010)) == rw.RWKV_ERR_ARG                  # xk inside x
+    assert shift(xr=p(0x400010)) == rw.RWKV_ERR_ARG                  # xr inside xk
+    assert shift(x_last=p(0x100000)) == rw.RWKV_ERR_ARG              # x_last on top of x
+    assert shift(x_prev=p(0x700000), x_last=p(0x700002)) == rw.RWKV_ERR_ARG  # partial overlap
+    assert shift(x_prev=p(0x700000), xk=p(0x700000)) == rw.RWKV_ERR_ARG
+
+
+def gate(n=64, r=p(0x100000), kv=p(0x200000), res=p(0x300000), y=p(0x400000), i=1, o=1):
+    return L.rwkv4_channelmix_gate(n, r, kv, res, y, i, o, None)
+
+
+def test_channelmix_gate_validation():
+    assert gate(n=-1) == rw.RWKV_ERR_ARG
+    assert gate(n=1 << 50) == rw.RWKV_ERR_ARG
+    assert gate(i=4) == rw.RWKV_ERR_DTYPE and gate(o=-2) == rw.RWKV_ERR_DTYPE
+    assert gate(r=None) == rw.RWKV_ERR_ARG and gate(kv=None) == rw.RWKV_ERR_ARG
+    assert gate(y=None) == rw.RWKV_ERR_ARG
+    assert gate(r=p(0x100001)) == rw.RWKV_ERR_ALIGN
+    assert gate(i=0, res=p(0x300002)) == rw.RWKV_ERR_ALIGN
+    assert gate(o=0, y=p(0x400002)) == rw.RWKV_ERR_ALIGN
+    assert gate(y=p(0x100000)) == rw.RWKV_ERR_ARG                    # y on top of r
+    assert gate(y=p(0x200010)) == rw.RWKV_ERR_ARG                    # y inside kv
+    assert gate(y=p(0x300010)) == rw.RWKV_ERR_ARG                    # y partly over the residual
+    assert gate(i=1, o=0, y=p(0x300000)) == rw.RWKV_ERR_ARG          # in place needs equal dtypes

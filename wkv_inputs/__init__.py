@@ -49,7 +49,7 @@ LN_EPS = 1e-5
 class Workload:
     index: int
     name: str
-    kind: str            # "forward" | "timemix" | "step"
+    kind: str            # "forward" | "timemix" | "step" | "shift" | "gate"
     B: int
     T: int
     C: int
@@ -73,6 +73,10 @@ WORKLOADS = {
                 256, 1, 5120, "f16", "f16", gated=True, prior=True, layers=40),
     4: Workload(4, "long-sequence chunked scan B1 T65536 C2048 f16->f32", "forward",
                 1, 65536, 2048, "f16", "f32", k_sigma=math.sqrt(2.0)),
+    5: Workload(5, "rwkv4-14b time-mix prologue: ln1 + token shift -> xk, xv, xr B1 T1024 C5120 f16",
+                "shift", 1, 1024, 5120, "f16", "f16", prior=True),
+    6: Workload(6, "rwkv4-14b channel-mix gate + residual B1 T1024 C5120 f16", "gate",
+                1, 1024, 5120, "f16", "f16"),
 }
 
 _NP = {"f32": np.float32, "f16": np.float16}
@@ -189,6 +193,10 @@ def workload_inputs(index: int, seed: int | None = None, **shape):
         layers = shape.get("layers", wl.layers)
         return [step_layer(l, B, C, seed=s, in_dtype=wl.in_dtype, index=index)
                 for l in range(layers)]
+    if wl.kind == "shift":
+        return shift_mix_case(B, T, C, seed=s, dtype=wl.in_dtype, prior=wl.prior, index=index)
+    if wl.kind == "gate":
+        return gate_case(B * T * C, seed=s, in_dtype=wl.in_dtype, out_dtype=wl.out_dtype, index=index)
     raise ValueError(wl.kind)
 
 
