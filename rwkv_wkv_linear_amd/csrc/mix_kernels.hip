@@ -63,6 +63,13 @@ __device__ __forceinline__ void ld8(const T *p, bool vec, int cnt, float (&f)[8]
     }
 }
 
+// Outputs are written once and never read back by the launch: streaming (non-temporal) stores,
+// so the lines do not linger dirty in L2 for the end-of-kernel write-back.
+template <typename V>
+__device__ __forceinline__ void st_stream(V *p, V v) {
+    __builtin_nontemporal_store(v, p);
+}
+
 // Store of 8 elements, rounded to nearest-even for 2-byte types.
 template <typename T>
 __device__ __forceinline__ void st8(T *p, bool vec, int cnt, const float (&f)[8]) {
@@ -74,18 +81,18 @@ __device__ __forceinline__ void st8(T *p, bool vec, int cnt, const float (&f)[8]
                 a[i] = f[i];
                 b[i] = f[4 + i];
             }
-            reinterpret_cast<f4v *>(p)[0] = a;
-            reinterpret_cast<f4v *>(p)[1] = b;
+            st_stream(reinterpret_cast<f4v *>(p), a);
+            st_stream(reinterpret_cast<f4v *>(p) + 1, b);
         } else {
             typename Vec8<T>::type a;
 #pragma unroll
             for (int i = 0; i < 8; ++i) a[i] = (T)f[i];
-            *reinterpret_cast<typename Vec8<T>::type *>(p) = a;
+            st_stream(reinterpret_cast<typename Vec8<T>::type *>(p), a);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (i < cnt) p[i] = (T)f[i];
+            if (i < cnt) st_stream(p + i, (T)f[i]);
     }
 }
 

@@ -125,6 +125,14 @@ __device__ __forceinline__ typename Raw<T>::type load4(const T *p, int64_t off, 
     return r;
 }
 
+// Every output of these kernels is written once and never read back by the launch that writes
+// it: streaming (non-temporal) stores keep the written lines from lingering dirty in L2, where
+// the end-of-kernel write-back would otherwise flush them after the last workgroup.
+template <typename V>
+__device__ __forceinline__ void st_stream(V *p, V v) {
+    __builtin_nontemporal_store(v, p);
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T *p, int64_t off, int nch, bool vec, const float (&x)[4]) {
     using R = typename Raw<T>::type;
@@ -133,12 +141,12 @@ __device__ __forceinline__ void store4(T *p, int64_t off, int nch, bool vec, con
             R r;
 #pragma unroll
             for (int q = 0; q < 4; ++q) r[q] = (T)x[q];  // fp16: round to nearest even
-            *reinterpret_cast<R *>(p + off) = r;
+            st_stream(reinterpret_cast<R *>(p + off), r);
         }
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (q < nch) p[off + q] = (T)x[q];
+            if (q < nch) st_stream(p + off + q, (T)x[q]);
     }
 }
 
@@ -260,16 +268,16 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
             Bq[q] = s[q].b;
             P[q] = st_logmax(s[q], w[q]);
         }
-        *reinterpret_cast<f4 *>(a.state_out + sc) = A;
-        *reinterpret_cast<f4 *>(a.state_out + BC + sc) = Bq;
-        *reinterpret_cast<f4 *>(a.state_out + 2 * BC + sc) = P;
+        st_stream(reinterpret_cast<f4 *>(a.state_out + sc), A);
+        st_stream(reinterpret_cast<f4 *>(a.state_out + BC + sc), Bq);
+        st_stream(reinterpret_cast<f4 *>(a.state_out + 2 * BC + sc), P);
     } else if (a.state_out) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (q < nch) {
-                a.state_out[sc + q] = s[q].a;
-                a.state_out[BC + sc + q] = s[q].b;
-                a.state_out[2 * BC + sc + q] = st_logmax(s[q], w[q]);
+                st_stream(a.state_out + sc + q, s[q].a);
+                st_stream(a.state_out + BC + sc + q, s[q].b);
+                st_stream(a.state_out + 2 * BC + sc + q, st_logmax(s[q], w[q]));
             }
     }
     if constexpr (MODE == MODE_TIMEMIX) {
@@ -524,8 +532,8 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
                 if constexpr (MIX) {
                     const float xx = (float)gh[j];
                     const unsigned off = i * Cu + (unsigned)lane;
-                    if (xkrow) xkrow[off] = (TIn)fmaf(mk, xx - xs, xs);
-                    if (xvrow) xvrow[off] = (TIn)fmaf(mv, xx - xs, xs);
+                    if (xkrow) st_stream(xkrow + off, (TIn)fmaf(mk, xx - xs, xs));
+                    if (xvrow) st_stream(xvrow + off, (TIn)fmaf(mv, xx - xs, xs));
                     xs = xx;
                 }
                 gbx = fmaf(gb, (float)gh[j], 0.f);
@@ -534,7 +542,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
             if constexpr (STAGE)
                 ystage[i * CW + lane] = yv;
             else
-                yrow[i * Cu + (unsigned)lane] = yv;
+                st_stream(yrow + i * Cu + (unsigned)lane, yv);
             nn = fmaf(ew, nn, P);
             dd = fmaf(ew, dd, X);
         }
@@ -551,7 +559,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
             for (int j = 0; j < LB / RPI; ++j) {
                 const int r = h + j * RPI + rs;
                 const f4 chunk = *reinterpret_cast<const f4 *>(ystage + r * CW + q * CH16);
-                *reinterpret_cast<f4 *>(yrow + r * Cu + q * CH16) = chunk;
+                st_stream(reinterpret_cast<f4 *>(yrow + r * Cu + q * CH16), chunk);
             }
         }
     }
@@ -809,10 +817,10 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
                 }
                 const float yv = num * rcp(den * g);
                 if (i < nval) {
-                    Y[base + i * C] = (TOut)yv;
+                    st_stream(Y + base + i * C, (TOut)yv);
                     if constexpr (MODE == MODE_TIMEMIX) {
-                        if (XKO) XKO[base + i * C] = (TIn)fmaf(mk, xx - xs, xs);
-                        if (XVO) XVO[base + i * C] = (TIn)fmaf(mv, xx - xs, xs);
+                        if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
+                        if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
                     }
                 }
                 if constexpr (MODE == MODE_TIMEMIX) xs = (i < nval) ? xx : xs;
@@ -837,11 +845,11 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
                 if constexpr (MODE == MODE_TIMEMIX) {
                     const float xx = (float)gr[i * CW];
                     g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
-                    if (XKO) XKO[base + i * C] = (TIn)fmaf(mk, xx - xs, xs);
-                    if (XVO) XVO[base + i * C] = (TIn)fmaf(mv, xx - xs, xs);
+                    if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
+                    if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
                     xs = xx;
                 }
-                Y[base + i * C] = (TOut)(num * rcp(den * g));
+                st_stream(Y + base + i * C, (TOut)(num * rcp(den * g)));
                 absorb(s2, wc, kk, vv);
             }
         }
@@ -851,12 +859,12 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     // Phase F: the lane holding token T-1 writes the final state (and x_last).
     if (nval > 0 && t0 + nval == a.T) {
         if (a.state_out) {
-            a.state_out[b * C + c] = fin.a;
-            a.state_out[BC + b * C + c] = fin.b;
-            a.state_out[2 * BC + b * C + c] = st_logmax(fin, wc);
+            st_stream(a.state_out + b * C + c, fin.a);
+            st_stream(a.state_out + BC + b * C + c, fin.b);
+            st_stream(a.state_out + 2 * BC + b * C + c, st_logmax(fin, wc));
         }
         if constexpr (MODE == MODE_TIMEMIX) {
-            if (a.x_last) static_cast<TIn *>(a.x_last)[b * C + c] = (TIn)xs;
+            if (a.x_last) st_stream(static_cast<TIn *>(a.x_last) + b * C + c, (TIn)xs);
         }
     }
 }
