@@ -42,24 +42,33 @@ template <> struct Vec8<__bf16> { using type = b8; };
 
 // 8 consecutive elements starting at p: one 16-byte load (two for fp32) when vec, else
 // per-element loads of the first cnt (the rest read as 0).
-template <typename T>
+// With NT the loads carry the non-temporal (streaming) hint: for data read for the last time.
+template <typename V, bool NT>
+__device__ __forceinline__ V ldv(const V *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <typename T, bool NT = false>
 __device__ __forceinline__ void ld8(const T *p, bool vec, int cnt, float (&f)[8]) {
     if (vec) {
         if constexpr (sizeof(T) == 4) {
-            const f4v a = reinterpret_cast<const f4v *>(p)[0], b = reinterpret_cast<const f4v *>(p)[1];
+            const f4v a = ldv<f4v, NT>(reinterpret_cast<const f4v *>(p)), b = ldv<f4v, NT>(reinterpret_cast<const f4v *>(p) + 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 f[i] = a[i];
                 f[4 + i] = b[i];
             }
         } else {
-            const typename Vec8<T>::type a = *reinterpret_cast<const typename Vec8<T>::type *>(p);
+            const typename Vec8<T>::type a = ldv<typename Vec8<T>::type, NT>(reinterpret_cast<const typename Vec8<T>::type *>(p));
 #pragma unroll
             for (int i = 0; i < 8; ++i) f[i] = (float)a[i];
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = i < cnt ? (float)p[i] : 0.f;
+        for (int i = 0; i < 8; ++i) f[i] = i < cnt ? (float)ldv<T, NT>(p + i) : 0.f;
     }
 }
 
@@ -107,26 +116,26 @@ template <> struct Raw8<float> {
     __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
-template <typename T>
+template <typename T, bool NT = false>
 __device__ __forceinline__ Raw8<T> ldraw(const T *p, bool vec, int cnt) {
     Raw8<T> r;
     if constexpr (sizeof(T) == 4) {
         if (vec) {
-            r.a = reinterpret_cast<const f4v *>(p)[0];
-            r.b = reinterpret_cast<const f4v *>(p)[1];
+            r.a = ldv<f4v, NT>(reinterpret_cast<const f4v *>(p));
+            r.b = ldv<f4v, NT>(reinterpret_cast<const f4v *>(p) + 1);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                r.a[i] = i < cnt ? p[i] : 0.f;
-                r.b[i] = 4 + i < cnt ? p[4 + i] : 0.f;
+                r.a[i] = i < cnt ? ldv<float, NT>(p + i) : 0.f;
+                r.b[i] = 4 + i < cnt ? ldv<float, NT>(p + 4 + i) : 0.f;
             }
         }
     } else {
         if (vec) {
-            r.v = *reinterpret_cast<const typename Vec8<T>::type *>(p);
+            r.v = ldv<typename Vec8<T>::type, NT>(reinterpret_cast<const typename Vec8<T>::type *>(p));
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) r.v[i] = i < cnt ? p[i] : T(0);
+            for (int i = 0; i < 8; ++i) r.v[i] = i < cnt ? ldv<T, NT>(p + i) : T(0);
         }
     }
     return r;
@@ -262,7 +271,7 @@ __global__ void __launch_bounds__(kShiftThreads) shift_mix_kernel(ShiftArgs a) {
         Raw8<T> xr[kRowsPerBlock], xp, xl;
 #pragma unroll
         for (int r = 0; r < kRowsPerBlock; ++r)
-            if (r < rows) xr[r] = ldraw(col + (t0 + r) * C, vec, cnt);
+            if (r < rows) xr[r] = ldraw<T, true>(col + (t0 + r) * C, vec, cnt);  // the rows' last reads
         if (t0 > 0)
             xp = ldraw(col + (t0 - 1) * C, vec, cnt);
         else if (a.x_prev)
@@ -340,9 +349,9 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
         const int64_t i0 = 8 * j;
         const int cnt = (int)std::min<int64_t>(8, a.n - i0);
         float r[8], kv[8], res[8], y[8];
-        ld8(R + i0, vec, cnt, r);
-        ld8(KV + i0, vec, cnt, kv);
-        if (RES) ld8(RES + i0, vec, cnt, res);
+        ld8<TIn, true>(R + i0, vec, cnt, r);
+        ld8<TIn, true>(KV + i0, vec, cnt, kv);
+        if (RES) ld8<TIn, true>(RES + i0, vec, cnt, res);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float g = kv[i] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * r[i]));

@@ -111,16 +111,18 @@ __device__ __forceinline__ void emit(const St &s, float w, float u, float k, flo
 
 // Four consecutive channels at element offset `off`; nch of them valid.  With vec
 // set, nch is 0 or 4 and the access is one aligned vector load.
+// Activations and states are read once per launch: the loads are streaming (non-temporal)
+// hints, so they do not displace reused lines (parameters, published tile states) from L2.
 template <typename T>
 __device__ __forceinline__ typename Raw<T>::type load4(const T *p, int64_t off, int nch, bool vec) {
     using R = typename Raw<T>::type;
     R r = {0, 0, 0, 0};
     if (vec) {
-        if (nch == 4) r = *reinterpret_cast<const R *>(p + off);
+        if (nch == 4) r = __builtin_nontemporal_load(reinterpret_cast<const R *>(p + off));
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (q < nch) r[q] = p[off + q];
+            if (q < nch) r[q] = __builtin_nontemporal_load(p + off + q);
     }
     return r;
 }
@@ -151,10 +153,11 @@ __device__ __forceinline__ void store4(T *p, int64_t off, int nch, bool vec, con
 }
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane l's
-// bytes land at lds + 16 l.  `lds` must be the same for the whole wave.
+// bytes land at lds + 16 l.  `lds` must be the same for the whole wave.  The rows are read
+// once: cache policy 2 is the non-temporal (streaming) hint.
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 2);
 }
 
 // L values of one channel, one per token, as loaded.
@@ -202,9 +205,9 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[q] = finite_decay(w[q]);
     if (a.state_in && vs) {
-        const f4 A = *reinterpret_cast<const f4 *>(a.state_in + sc);
-        const f4 Bq = *reinterpret_cast<const f4 *>(a.state_in + BC + sc);
-        const f4 P = *reinterpret_cast<const f4 *>(a.state_in + 2 * BC + sc);
+        const f4 A = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(a.state_in + sc));
+        const f4 Bq = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(a.state_in + BC + sc));
+        const f4 P = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(a.state_in + 2 * BC + sc));
 #pragma unroll
         for (int q = 0; q < 4; ++q) s[q] = st_load(A[q], Bq[q], P[q]);
     } else {
