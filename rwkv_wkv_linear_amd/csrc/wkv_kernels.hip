@@ -392,8 +392,9 @@ constexpr float kGuardState = 60.f;
 
 // Phase A of a tile: wave wv stages its L rows (tokens t0 .. t0+L-1 of the tile) of each
 // of the NT tensors in src into LDS rows[NT][TW][64].  With 16-byte vectors (vec16) each
-// global_load_lds_dwordx4 moves RPI whole 128-B (fp16) or 256-B (fp32) rows, and no VGPR holds
-// a load in flight; otherwise each lane loads its own channel in rolled batches of 4 rows (a
+// global_load_lds_dwordx4 moves RPI whole 128-B (fp16) or 256-B (fp32) rows, no VGPR holds
+// a load in flight, and the instructions go out RPI rows of every tensor at a time (the
+// staged summary waits for them group by group); otherwise each lane loads its own channel in rolled batches of 4 rows (a
 // rare path, kept from setting the kernel's register footprint).  Rows past T and chunks past
 // C read a valid clamped address whose data is never used.
 template <typename TIn, int NT, int L>
@@ -408,10 +409,12 @@ __device__ __forceinline__ void stage_rows(const TIn *const *src, TIn *rows, int
         const int q = lane % CHUNKS, rsub = lane / CHUNKS;
         int64_t cq = ct * CW + q * CH16;
         if (cq >= C) cq = 0;
+        // row-group major (rows j*RPI .. of every tensor, then the next rows): loads complete
+        // in issue order, so the summary can take each group of rows as it lands
 #pragma unroll
-        for (int tsr = 0; tsr < NT; ++tsr) {
+        for (int j = 0; j < L / RPI; ++j) {
 #pragma unroll
-            for (int j = 0; j < L / RPI; ++j) {
+            for (int tsr = 0; tsr < NT; ++tsr) {
                 const int r = wv * L + j * RPI;
                 const int64_t t = std::min<int64_t>(tile_t0 + r + rsub, T - 1);
                 dma16(src[tsr] + (b * T + t) * C + cq, rows + ((size_t)tsr * TW + r) * CW);
@@ -492,6 +495,65 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
             if (i < nval) absorb(sum, wc, xk[i], vb[i]);
     }
     return sum;
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Phase B for a full wave whose rows arrive by 16-byte DMA in row-group order (stage_rows):
+// the summary takes 8 tokens at a time as soon as they have landed, while the later groups are
+// still in flight.  Weights are scaled by the largest key of the first group, mref, instead of
+// the wave's largest key (unknown until the last group lands): with the key spread of the wave
+// at most kGuardSpread every weight e^{k - mref} stays a normal fp32 number, and the guard is
+// decided after the last group exactly as in wave_summary.  Loads complete in issue order, so
+// when at most (instructions issued after group g) are outstanding, group g is in LDS.
+template <typename TIn, int NT, int L>
+__device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, float ew, float uc, float &mref,
+                                                  bool &fast, float (&Xs)[L]) {
+    constexpr int CW = kTileChannels, G = 8, NG = L / G;
+    constexpr int RPI = 64 / (CW / (16 / (int)sizeof(TIn)));  // rows per DMA instruction
+    constexpr int IPG = NT * (G / RPI);                       // DMA instructions per group
+    static_assert(L % G == 0 && G % RPI == 0, "groups are whole DMA instructions");
+    float nn = 0.f, dd = 0.f, kmax = -INFINITY, kmin = INFINITY, m = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (NG - 1 - g == 3) wait_vmcnt<3 * IPG>();
+        else if (NG - 1 - g == 2) wait_vmcnt<2 * IPG>();
+        else if (NG - 1 - g == 1) wait_vmcnt<IPG>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_wave_barrier();
+        float xk[G], vb[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            xk[i] = (float)kr[(g * G + i) * CW];
+            vb[i] = (float)vr[(g * G + i) * CW];
+        }
+        float gmax = xk[0], gmin = xk[0];
+#pragma unroll
+        for (int i = 1; i < G; ++i) {
+            gmax = fmaxf(gmax, xk[i]);
+            gmin = fminf(gmin, xk[i]);
+        }
+        if (g == 0) m = gmax;
+        kmax = fmaxf(kmax, gmax);
+        kmin = fminf(kmin, gmin);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const float X = ex(xk[i] - m);
+            Xs[g * G + i] = X;  // kept for the emit phase
+            nn = fmaf(ew, nn, X * vb[i]);
+            dd = fmaf(ew, dd, X);
+        }
+    }
+    static_assert(NG <= 4, "at most four groups per wave");
+    fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
+    mref = m;
+    return St{nn, dd, m, 0.f};
 }
 
 // Linear-space emit of one wave's L tokens when all of them are valid: y_i from the running
@@ -654,12 +716,10 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         }
     }
 
-    // Phase A: stage this wave's rows.
-    {
-        const TIn *src[3] = {K, V, GR};
-        stage_rows<TIn, NT, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
-    }
-    // per-channel parameters (and the time-mix token before wave 0's first) load meanwhile
+    // Per-channel parameters, the time-mix token before the tile and the prior state are loaded
+    // before the rows: vector loads complete in issue order, so they are in registers before the
+    // first group of rows, and the staged summary's counted waits see only the row loads after
+    // them.  The empty asm keeps the compiler from moving memory accesses across it.
     const float w_raw = a.w[cs], u_raw = a.u[cs];
     const float wc = cok ? finite_decay(w_raw) : 0.f;
     const float uc = cok ? u_raw : 0.f;
@@ -676,11 +736,17 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         mk = cok ? mk_raw : 0.f;
         mv = cok ? mv_raw : 0.f;
     }
+    if (tt == 0 && a.state_in && cok)
+        prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
+    asm volatile("" ::: "memory");
+
+    // Phase A: stage this wave's rows.
+    {
+        const TIn *src[3] = {K, V, GR};
+        stage_rows<TIn, NT, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
+    }
     const float ew = ex(wc), eu = ex(uc);
-    if (tt == 0) {
-        if (a.state_in && cok)
-            prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
-    } else if constexpr (PREFIX == PREFIX_AGGS) {
+    if (PREFIX == PREFIX_AGGS && tt > 0) {
         sF[(0 * S + wv) * CW + lane] = part.a;
         sF[(1 * S + wv) * CW + lane] = part.b;
         sF[(2 * S + wv) * CW + lane] = part.k;
@@ -697,18 +763,33 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         }
         __syncthreads();  // the wave summaries reuse sF next
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-    __builtin_amdgcn_wave_barrier();
-
     const TIn *kr = rows + ((size_t)0 * TW + wv * L) * CW + lane;
     const TIn *vr = rows + ((size_t)1 * TW + wv * L) * CW + lane;
     const TIn *gr = rows + ((size_t)2 * TW + wv * L) * CW + lane;
 
-    // Phase B: summary of the wave's tokens from the empty state.
-    float kmax;
+    // Phase B: summary of the wave's tokens from the empty state.  A full wave whose rows come
+    // by 16-byte DMA takes them group by group as they land (wave-uniform choice); lanes past C
+    // then drop their summary (their rows are a copy of channel 0).
+    float kmax;   // the weights' reference key: the largest key (or the first group's, staged)
     bool fast;
     float Xs[L];  // the weights e^{k_i - kmax} of a full wave on the fast path
-    const St sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
+    St sum;
+    if (a.vec16 && wlen == L) {
+        sum = wave_summary_staged<TIn, NT, L>(kr, vr, ew, uc, kmax, fast, Xs);
+        if (!cok) {
+            sum = st_empty();
+            fast = false;
+        } else if (!fast) {
+            // outside the linear-space guard: the exact per-token recurrence (all rows landed)
+            sum = st_empty();
+#pragma unroll 1
+            for (int i = 0; i < L; ++i) absorb(sum, wc, (float)kr[i * CW], (float)vr[i * CW]);
+        }
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+        __builtin_amdgcn_wave_barrier();
+        sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
+    }
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
