@@ -512,9 +512,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // at most kGuardSpread every weight e^{k - mref} stays a normal fp32 number, and the guard is
 // decided after the last group exactly as in wave_summary.  Loads complete in issue order, so
 // when at most (instructions issued after group g) are outstanding, group g is in LDS.
-template <typename TIn, int NT, int L>
-__device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, float ew, float uc, float &mref,
-                                                  bool &fast, float (&Xs)[L]) {
+//
+// With a gate (MODE_GATED, MODE_TIMEMIX) it also forms every token's gate factor
+// G_i = 1 + e^{-r_i} (r_i = xr_i = mr x_i + (1 - mr) x_{i-1} for the time mix, in base 2 as
+// ga x_i + gb x_{i-1}; xprev is the token before the wave), which does not depend on the state.
+template <typename TIn, int NT, int L, int MODE, bool GATE>
+__device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, const TIn *gr, float ew, float uc,
+                                                  float ga, float gb, float xprev, float &mref, bool &fast,
+                                                  float (&Xs)[L], float (&Gs)[L]) {
     constexpr int CW = kTileChannels, G = 8, NG = L / G;
     constexpr int RPI = 64 / (CW / (16 / (int)sizeof(TIn)));  // rows per DMA instruction
     constexpr int IPG = NT * (G / RPI);                       // DMA instructions per group
@@ -549,6 +554,18 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
             nn = fmaf(ew, nn, X * vb[i]);
             dd = fmaf(ew, dd, X);
         }
+        if constexpr (GATE && MODE == MODE_GATED) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) Gs[g * G + i] = 1.f + __builtin_amdgcn_exp2f(-kLog2e * (float)gr[(g * G + i) * CW]);
+        }
+        if constexpr (GATE && MODE == MODE_TIMEMIX) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float xx = (float)gr[(g * G + i) * CW];
+                Gs[g * G + i] = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xprev));
+                xprev = xx;
+            }
+        }
     }
     static_assert(NG <= 4, "at most four groups per wave");
     fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
@@ -565,10 +582,12 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
 // 16-byte stores (yrow 16-byte aligned, all 64 channels in range), MIX
 // writes the time-mix xk/xv rows.  Xs holds the weights e^{k_i - kmax} from the summary
 // phase; vr, gr point at the lane's first staged row.
-template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
-__device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, const TIn *gr, float eu,
-                                          float ew, float ga, float gb, float mk, float mv, float &xs, float &nn,
-                                          float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
+// With PRE the gate factors G_i = 1 + e^{-r_i} come precomputed in Gs (the summary phase
+// formed them while the rows were still landing) and the gate costs one multiply per token.
+template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX, bool PRE>
+__device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs)[L], const TIn *vr, const TIn *gr,
+                                          float eu, float ew, float ga, float gb, float mk, float mv, float &xs,
+                                          float &nn, float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
                                           unsigned Cu, int lane) {
     constexpr int CW = kTileChannels;
     constexpr int LB = 8;  // rows read from LDS per batch, to bound the registers they occupy
@@ -578,10 +597,11 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 #pragma unroll
     for (int h = 0; h < L; h += LB) {
         TIn vh[LB], gh[LB];
+        constexpr bool kNeedX = MODE != MODE_PLAIN && (!PRE || MIX);  // x (or r) rows still read here
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             vh[j] = vr[(h + j) * CW];
-            gh[j] = (MODE == MODE_PLAIN) ? TIn(0) : gr[(h + j) * CW];
+            gh[j] = kNeedX ? gr[(h + j) * CW] : TIn(0);
         }
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
@@ -591,9 +611,10 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
             const float num = fmaf(eu, P, nn);
             const float den = fmaf(eu, X, dd);
             float dg = den;  // den * (1 + e^{-r})
-            if constexpr (MODE == MODE_GATED) dg = fmaf(den, __builtin_amdgcn_exp2f(-kLog2e * (float)gh[j]), den);
+            if constexpr (PRE && MODE != MODE_PLAIN) dg = den * Gs[i];
+            if constexpr (!PRE && MODE == MODE_GATED) dg = fmaf(den, __builtin_amdgcn_exp2f(-kLog2e * (float)gh[j]), den);
             if constexpr (MODE == MODE_TIMEMIX) {
-                dg = fmaf(den, __builtin_amdgcn_exp2f(fmaf(ga, (float)gh[j], gbx)), den);
+                if constexpr (!PRE) dg = fmaf(den, __builtin_amdgcn_exp2f(fmaf(ga, (float)gh[j], gbx)), den);
                 if constexpr (MIX) {
                     const float xx = (float)gh[j];
                     const unsigned off = i * Cu + (unsigned)lane;
@@ -601,7 +622,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
                     if (xvrow) st_stream(xvrow + off, (TIn)fmaf(mv, xx - xs, xs));
                     xs = xx;
                 }
-                gbx = fmaf(gb, (float)gh[j], 0.f);
+                if constexpr (!PRE) gbx = fmaf(gb, (float)gh[j], 0.f);
             }
             const TOut yv = (TOut)(num * rcp(dg));
             if constexpr (STAGE)
@@ -746,6 +767,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         stage_rows<TIn, NT, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
     }
     const float ew = ex(wc), eu = ex(uc);
+    // gate argument in base 2: -log2(e) * (mr x + (1 - mr) xs)
+    const float ga = -kLog2e * mr, gb = -kLog2e * (1.f - mr);
     if (PREFIX == PREFIX_AGGS && tt > 0) {
         sF[(0 * S + wv) * CW + lane] = part.a;
         sF[(1 * S + wv) * CW + lane] = part.b;
@@ -770,12 +793,19 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     // Phase B: summary of the wave's tokens from the empty state.  A full wave whose rows come
     // by 16-byte DMA takes them group by group as they land (wave-uniform choice); lanes past C
     // then drop their summary (their rows are a copy of channel 0).
+    // 32-token waves with a receptance input also keep the gate factors 1 + e^{-r} of their
+    // tokens (formed during the summary, while rows are still landing, when staged).  The time
+    // mix forms its gate in the emit instead: its first token's r needs the previous wave's last
+    // row, which the summary phase may not wait for (measured slower when each wave fetched it).
+    constexpr bool PRE = L == 32 && MODE == MODE_GATED;
     float kmax;   // the weights' reference key: the largest key (or the first group's, staged)
     bool fast;
     float Xs[L];  // the weights e^{k_i - kmax} of a full wave on the fast path
+    float Gs[L];  // gate factors (PRE)
     St sum;
-    if (a.vec16 && wlen == L) {
-        sum = wave_summary_staged<TIn, NT, L>(kr, vr, ew, uc, kmax, fast, Xs);
+    const bool staged = a.vec16 && wlen == L;
+    if (staged) {
+        sum = wave_summary_staged<TIn, NT, L, MODE, PRE>(kr, vr, gr, ew, uc, ga, gb, xs, kmax, fast, Xs, Gs);
         if (!cok) {
             sum = st_empty();
             fast = false;
@@ -789,6 +819,15 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
         __builtin_amdgcn_wave_barrier();
         sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
+        if constexpr (PRE) {
+            float xp = xs;
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const float r = (float)gr[i * CW];
+                Gs[i] = 1.f + __builtin_amdgcn_exp2f(MODE == MODE_GATED ? -kLog2e * r : fmaf(ga, r, gb * xp));
+                xp = r;
+            }
+        }
     }
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
@@ -852,8 +891,6 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     if constexpr (MODE == MODE_TIMEMIX) {
         if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
     }
-    // gate argument in base 2: -log2(e) * (mr x + (1 - mr) xs)
-    const float ga = -kLog2e * mr, gb = -kLog2e * (1.f - mr);
     const float pst = st_logmax(st, wc);
     St fin;
     if (fast && pst - kmax <= kGuardState) {
@@ -872,8 +909,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
             TOut *yrow = Y + row0;
             TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
 #define RWKV_EMIT(STAGE, MIX)                                                                          \
-    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow,       \
-                                              xkrow, xvrow, ystage, Cu, lane)
+    emit_full<TIn, TOut, MODE, L, STAGE, MIX, PRE>(Xs, Gs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
+                                                   xkrow, xvrow, ystage, Cu, lane)
             if constexpr (MODE == MODE_TIMEMIX) {
                 if (stage_y) {
                     if (mix) RWKV_EMIT(true, true); else RWKV_EMIT(true, false);
