@@ -34,9 +34,10 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
     note(f"forward {label} B={B} T={T} C={C} in={case['in_dtype']} out={odt} "
          f"gated={case.get('r') is not None} prior={case.get('state_in') is not None} "
          f"algo={algo} chunk={chunk_len}")
-    rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
+    idt = case["in_dtype"]
+    rw.rwkv4_wkv_forward(to_dev(case["k"], idt), to_dev(case["v"], idt), to_dev(case["w"]), to_dev(case["u"]),
                          y=y, state_in=to_dev(case.get("state_in")), state_out=so,
-                         r=to_dev(case.get("r")), chunk_len=chunk_len, algo=algo)
+                         r=to_dev(case.get("r"), idt), chunk_len=chunk_len, algo=algo)
     torch().cuda.synchronize()
     assert canary_ok(yfull, B * T * C), "write past the end of y"
     if so is not None:
@@ -187,6 +188,25 @@ def test_wide_key_spread():
         y, s = run(case, algo, chunk, label="wide spread")
         check_output(y, ref, TOL["f32"], f"spread {algo}/{chunk}")
         check_state(s, ref, TOL["f32"], f"spread {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("in_dt", ["f16", "bf16"])
+def test_wide_key_spread_2byte_staged(in_dt):
+    """2-byte keys over +-60 nats on 128-token tiles: the staged summary (rows folded group by
+    group as they land) must fall back to the exact recurrence for waves outside the guard,
+    also when only some lanes or some groups are outside it, and in a ragged last tile."""
+    case = wi.forward_case(2, 1000, 192, seed=51, in_dtype=in_dt, out_dtype="f32", gated=True, prior=True)
+    g = np.random.default_rng(51)
+    k = g.uniform(-60, 60, case["k"].shape)
+    k[:, :, :64] = g.normal(0, 1, k[:, :, :64].shape)          # first channel tile inside the guard
+    k[:, 300:340, 64:128] = g.uniform(-60, 60, (2, 40, 64))     # a burst in one group of one tile
+    k[:, :, 64:128] = np.where(np.arange(1000)[None, :, None] < 300, g.normal(0, 1, (2, 1000, 64)), k[:, :, 64:128])
+    case["k"] = wi._as(k, in_dt)
+    ref = oracle.forward(case)
+    for algo, chunk in (("chunked", 128), ("two_pass", 128)):
+        y, s = run(case, algo, chunk, label=f"wide spread {in_dt}")
+        check_output(y, ref, TOL[in_dt], f"spread {in_dt} {algo}/{chunk}")
+        check_state(s, ref, TOL[in_dt], f"spread {in_dt} {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("algo", ["chunked", "two_pass"])
