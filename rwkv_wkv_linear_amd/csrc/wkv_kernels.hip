@@ -382,6 +382,22 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 //   incoming state scale p - kmax <= 60, so it cannot overflow.
 // A lane outside the guard runs the exact per-token max-trick instead (same results within
 // rounding; the tests drive both paths).
+// Workgroups are handed to the eight XCDs round-robin by index, so blockIdx % 8 picks a
+// workgroup's XCD.  When nCT is a multiple of 8, the plain order (r = b * nCT + ct) gives each
+// XCD every eighth chain, all in the same 128-byte column of every 1 KB of each row, and the
+// column at bytes 384-511 loads about a sixth slower on MI355X (measured: the slowness moves
+// with the column, not the XCD), so one XCD ends well after the rest.  Index r then goes to
+// chain (r % 8) * (B * nCT / 8) + r / 8 instead: every time tile of a chain still runs on one
+// XCD, and each XCD runs a contiguous range of chains that spans all columns.  Otherwise
+// consecutive batch rows already shift the column an XCD sees, and the plain order stays
+// (measured faster there).
+__device__ __forceinline__ void tile_chain(int64_t rem, int64_t BCT, int nCT, int64_t &b, int64_t &ct) {
+    constexpr int kXcds = 8;
+    const int64_t r = (nCT % kXcds == 0) ? (rem % kXcds) * (BCT / kXcds) + rem / kXcds : rem;
+    b = r / nCT;
+    ct = r - b * nCT;
+}
+
 // How a tile gets its incoming state: from its predecessors in the same launch (single
 // pass, decoupled look-back) or from tile aggregates a previous launch wrote (two passes).
 constexpr int PREFIX_LOOKBACK = 0, PREFIX_AGGS = 1;
@@ -653,8 +669,8 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs
 }
 
 // Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = S * L tokens),
-// blockIdx = tt * (B * nCT) + b * nCT + ct, so every tile a workgroup waits for has a
-// lower index and was dispatched earlier.  PREFIX selects where the tile's incoming state
+// blockIdx = tt * (B * nCT) + r with (b, ct) = tile_chain(r), so every tile a workgroup waits
+// for has a lower index and was dispatched earlier.  PREFIX selects where the tile's incoming state
 // comes from: the single-pass look-back (phase D) or the aggregates of a first pass.  Wave w of S = tokens tt*TW + w*L .. +L-1;
 // lane = channel ct*64 + lane.
 //
@@ -684,7 +700,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const int64_t BCT = a.B * nCT;
     const int64_t tt = blockIdx.x / BCT;
     const int64_t rem = blockIdx.x - tt * BCT;
-    const int64_t b = rem / nCT, ct = rem - b * nCT;
+    int64_t b, ct;
+    tile_chain(rem, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
     const bool cok = c < a.C;
     const int64_t tile_t0 = tt * TW;
@@ -1023,7 +1040,8 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     const int64_t BCT = a.B * nCT;
     const int64_t tt = blockIdx.x / BCT;  // < nTT - 1: every tile here is full
     const int64_t rem = blockIdx.x - tt * BCT;
-    const int64_t b = rem / nCT, ct = rem - b * nCT;
+    int64_t b, ct;
+    tile_chain(rem, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
     const bool cok = c < a.C;
     const int64_t tile_t0 = tt * TW, t0 = tile_t0 + (int64_t)wv * L;

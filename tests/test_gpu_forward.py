@@ -230,6 +230,18 @@ def test_split_sequence_carry(algo):
     check_state(host(st), ref, TOL["f32"], f"split carry {algo}")
 
 
+@pytest.mark.parametrize("B,T,C", [(3, 700, 512), (1, 900, 1024)])
+@pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)])
+def test_chain_order_across_xcds(B, T, C, algo, chunk):
+    # ceil(C / 64) a multiple of 8: workgroups map to (batch, channel tile)
+    # through the XCD-contiguous order (across batch rows for B = 3), with ragged last tiles
+    case = wi.forward_case(B, T, C, seed=53 + B, in_dtype="f16", gated=True, prior=True)
+    ref = oracle_forward(("xcd order", B, T, C), case)
+    y, st = run(case, algo, chunk, label="xcd order")
+    check_output(y, ref, TOL["f16"], f"xcd order B{B} T{T} C{C} {algo}/{chunk}", out_dtype="f16")
+    check_state(st, ref, TOL["f16"], f"xcd order B{B} T{T} C{C} {algo}/{chunk}")
+
+
 @pytest.mark.parametrize("algo", ["chunked", "two_pass"])
 def test_deterministic(algo):
     import rwkv_wkv_linear_amd as rw
