@@ -1215,10 +1215,10 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {
     const int64_t nCT = (C + kTileChannels - 1) / kTileChannels;
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
-    // words [tiles][4][64] u64 (one published state per tile, single pass) + one error word
-    // (padded to 256 B) + aggregates [tiles][64][4] fp32 (two passes).  The two regions are
-    // disjoint, so a float left by one algorithm can never pass for a tagged word.
-    return (size_t)(tiles * 4 * kTileChannels * 8 + 256 + tiles * kTileChannels * 4 * 4);
+    // a 256-byte header (the error word), then words [tiles][4][64] u64 (one published state
+    // per tile, single pass), then aggregates [tiles][64][4] fp32 (two passes).  The two
+    // regions are disjoint, so a float left by one algorithm can never pass for a tagged word.
+    return (size_t)(256 + tiles * 4 * kTileChannels * 8 + tiles * kTileChannels * 4 * 4);
 }
 
 void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
@@ -1227,9 +1227,13 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
     const int64_t nTT = (T + chunk_len - 1) / chunk_len;
     const int64_t tiles = B * nCT * nTT;
     char *p = static_cast<char *>(base);
-    ws->words = reinterpret_cast<uint64_t *>(p);
-    ws->err = reinterpret_cast<uint32_t *>(p + tiles * 4 * kTileChannels * 8);
-    ws->aggs = reinterpret_cast<float *>(p + tiles * 4 * kTileChannels * 8 + 256);
+    // The error word sits at a fixed place whatever the shape: it must read 0 unless a wait
+    // gave up, and one workspace serves calls of different shapes, whose word regions
+    // overwrite each other (a stale tagged word read as the error word would make every wait
+    // longer than 64 polls give up at once).
+    ws->err = reinterpret_cast<uint32_t *>(p);
+    ws->words = reinterpret_cast<uint64_t *>(p + 256);
+    ws->aggs = reinterpret_cast<float *>(p + 256 + tiles * 4 * kTileChannels * 8);
 }
 
 hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATCH(launch_seq_t, a, s); }

@@ -159,10 +159,10 @@ def test_workspace_bytes():
     a = rw.rwkv4_workspace_bytes(1, 65536, 2048, 64)
     b = rw.rwkv4_workspace_bytes(1, 65536, 2048, 1024)
     assert a > b > 0
-    # tiles * 4 fields * 64 channels * 8-byte tagged words, the error word, and the
-    # two-pass aggregates (tiles * 64 channels * 4 fp32)
+    # a 256-byte header (the error word), tiles * 4 fields * 64 channels * 8-byte
+    # tagged words, and the two-pass aggregates (tiles * 64 channels * 4 fp32)
     tiles = 32 * 1024
-    assert a == tiles * 4 * 64 * 8 + 256 + tiles * 64 * 16
+    assert a == 256 + tiles * 4 * 64 * 8 + tiles * 64 * 16
 
 
 def shift(B=2, T=8, C=16, x=p(0x100000), x_prev=None, x_last=None, ln_w=p(0x10000), ln_b=p(0x20000),
