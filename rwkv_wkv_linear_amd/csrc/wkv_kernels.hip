@@ -39,6 +39,8 @@
 #include "wkv_internal.h"
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace rwkvwkv {
 namespace {
@@ -387,13 +389,17 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 // XCD every eighth chain, all in the same 128-byte column of every 1 KB of each row, and the
 // column at bytes 384-511 loads about a sixth slower on MI355X (measured: the slowness moves
 // with the column, not the XCD), so one XCD ends well after the rest.  Index r then goes to
-// chain (r % 8) * (B * nCT / 8) + r / 8 instead: every time tile of a chain still runs on one
-// XCD, and each XCD runs a contiguous range of chains that spans all columns.  Otherwise
-// consecutive batch rows already shift the column an XCD sees, and the plain order stays
-// (measured faster there).
-__device__ __forceinline__ void tile_chain(int64_t rem, int64_t BCT, int nCT, int64_t &b, int64_t &ct) {
+// chain (r % 8) * (B * nCT / 8) + r / 8 instead: each XCD runs a contiguous range of chains
+// that spans all columns.  With rot set (calls of more workgroups than the GPU holds at once)
+// the ranges also rotate over the XCDs from one time tile to the next, (r + tt) % 8 in place
+// of r % 8; otherwise every time tile of a chain runs on one XCD.  Measured: rotation takes
+// the B1 T65536 C2048 call from 252 to 237 us and costs a one-round call (the 14B layer) 1.5
+// us.  When nCT is not a multiple of 8, consecutive batch rows already shift the column an XCD
+// sees, and the plain order stays (measured faster there).
+__device__ __forceinline__ void tile_chain(int64_t rem, int64_t tt, int rot, int64_t BCT, int nCT, int64_t &b,
+                                           int64_t &ct) {
     constexpr int kXcds = 8;
-    const int64_t r = (nCT % kXcds == 0) ? (rem % kXcds) * (BCT / kXcds) + rem / kXcds : rem;
+    const int64_t r = (nCT % kXcds == 0) ? ((rem + (rot ? tt : 0)) % kXcds) * (BCT / kXcds) + rem / kXcds : rem;
     b = r / nCT;
     ct = r - b * nCT;
 }
@@ -686,7 +692,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs
 // call is resident at once.
 template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
 __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorkspace &ws, int S, int nCT, int nTT,
-                                          int TW, int M) {
+                                          int TW, int M, int rot) {
     constexpr int CW = kTileChannels;
     constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -701,7 +707,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const int64_t tt = blockIdx.x / BCT;
     const int64_t rem = blockIdx.x - tt * BCT;
     int64_t b, ct;
-    tile_chain(rem, BCT, nCT, b, ct);
+    tile_chain(rem, tt, rot, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
     const bool cok = c < a.C;
     const int64_t tile_t0 = tt * TW;
@@ -1011,8 +1017,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
 // share a CU.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
-    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
-    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M);
+    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot) {
+    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot);
 }
 
 // 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
@@ -1020,8 +1026,8 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
 // occupancy each wave may hold its 32 weights in registers.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(256)
-    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M) {
-    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M);
+    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot) {
+    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1041,7 +1047,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     const int64_t tt = blockIdx.x / BCT;  // < nTT - 1: every tile here is full
     const int64_t rem = blockIdx.x - tt * BCT;
     int64_t b, ct;
-    tile_chain(rem, BCT, nCT, b, ct);
+    tile_chain(rem, tt, 0, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
     const bool cok = c < a.C;
     const int64_t tile_t0 = tt * TW, t0 = tile_t0 + (int64_t)wv * L;
@@ -1106,6 +1112,33 @@ __global__ void __launch_bounds__(256) wkv_passthrough_kernel(ForwardArgs a) {
     }
 }
 
+// Workgroups of a kernel the current device holds at once (occupancy x compute units), per
+// kernel, launch shape and device, computed once; 0 when the runtime cannot say.
+int64_t resident_slots(const void *kernel, int threads, size_t lds) {
+    constexpr int kMaxDevices = 64;
+    struct Entry {
+        const void *kernel;
+        int threads;
+        size_t lds;
+        int64_t slots;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry &e : cache[dev])
+        if (e.kernel == kernel && e.threads == threads && e.lds == lds) return e.slots;
+    int per_cu = 0, cus = 0;
+    int64_t slots = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        slots = (int64_t)per_cu * cus;
+    (void)hipGetLastError();  // a failed query leaves no sticky error behind
+    cache[dev].push_back(Entry{kernel, threads, lds, slots});
+    return slots;
+}
+
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_seq_t(const ForwardArgs &a, hipStream_t s) {
     const int64_t threads = a.B * ((a.C + 3) / 4);
@@ -1141,12 +1174,16 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    const void *kern = L == 32 ? reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>)
+                               : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
+    const int64_t slots = resident_slots(kern, 64 * S, lds);
+    const int rot = (slots > 0 && blocks > slots) ? 1 : 0;  // more than one round of workgroups
     if constexpr (L == 32)
         hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M);
+                           a, ws, S, nCT, nTT, chunk_len, M, rot);
     else
         hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M);
+                           a, ws, S, nCT, nTT, chunk_len, M, rot);
     return hipGetLastError();
 }
 
