@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "two_pass", "sequential"])
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the same-buffer (cache-warm) figure, e.g. under a profiler")
     ap.add_argument("--graph", action="store_true",
                     help="decode14b: capture the 40 layers' launches into one HIP graph and replay it "
                          "per step")
@@ -426,7 +428,7 @@ def main():
         "kernel_avg_us": launch_avg_ms * 1e3,
         "algorithmic_bytes_per_launch": su.launch_bytes,
     }
-    if len(su.sets) > 1 and not args.graph:
+    if len(su.sets) > 1 and not args.graph and not args.no_warm:
         # Context only, not the figure above: the same buffer set every launch, so the inputs
         # are served largely from the 256 MB Infinity Cache (warm).
         Kw = min(K, 200)
