@@ -157,6 +157,14 @@ __device__ __forceinline__ Moments merge(const Moments &a, const Moments &b) {
     return Moments{n, fmaf(d, fb, a.mean), a.m2 + b.m2 + d * d * a.n * fb};
 }
 
+// Sum over the 64 lanes of a wave; every lane gets the same value (each pair adds the same two
+// numbers, and addition commutes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
 // Moments of one row of C values, reduced over the 64 lanes of the calling wave; every lane
 // returns the row's result.
 template <typename T>
@@ -164,8 +172,57 @@ __device__ Moments row_moments(const T *row, int64_t C, bool vec, int lane) {
     // chunks in flight per lane: a whole row of up to 8192 (2-byte) or 4096 (fp32) channels is
     // requested at once, so the pass costs one memory latency
     constexpr int NF = sizeof(T) == 2 ? 16 : 8;
-    Moments acc{0.f, 0.f, 0.f};
     const int64_t nchunks = (C + 7) / 8;
+    if (nchunks <= NF * 64) {
+        // The whole row is in registers: two passes over them, the sum (-> the mean), then the
+        // squared deviations from the mean, each a per-lane tree of chunk sums and a butterfly
+        // of plain adds.  This is the textbook two-pass variance (no E[x^2] - E[x]^2
+        // cancellation), with one division per row instead of one per chunk.
+        Raw8<T> f[NF];
+        int cnt[NF];
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+            const int64_t j = m * 64 + lane;
+            cnt[m] = j < nchunks ? (int)std::min<int64_t>(8, C - 8 * j) : 0;
+            if (cnt[m] > 0) f[m] = ldraw(row + 8 * j, vec, cnt[m]);
+        }
+        float part[NF];
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+            float a = 0.f;
+            if (cnt[m] > 0)
+                a = ((f[m][0] + f[m][1]) + (f[m][2] + f[m][3])) + ((f[m][4] + f[m][5]) + (f[m][6] + f[m][7]));
+            part[m] = a;  // padding reads as 0
+        }
+#pragma unroll
+        for (int w = 1; w < NF; w *= 2)
+#pragma unroll
+            for (int m = 0; m + w < NF; m += 2 * w) part[m] += part[m + w];
+        const float mean = wave_sum(part[0]) / (float)C;
+        if constexpr (sizeof(T) == 2) {
+            // the packed values pass through an empty asm, so the second pass converts them
+            // again instead of holding every converted value in registers across the passes
+#pragma unroll
+            for (int m = 0; m < NF; ++m) asm volatile("" : "+v"(f[m].v));
+        }
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+            float q = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float d = f[m][i] - mean;
+                if (i < cnt[m]) q = fmaf(d, d, q);
+            }
+            part[m] = q;
+        }
+#pragma unroll
+        for (int w = 1; w < NF; w *= 2)
+#pragma unroll
+            for (int m = 0; m + w < NF; m += 2 * w) part[m] += part[m + w];
+        return Moments{(float)C, mean, wave_sum(part[0])};
+    }
+    // Longer rows stream through in passes of NF chunks, merged pairwise.
+    Moments acc{0.f, 0.f, 0.f};
     for (int64_t j0 = 0; j0 < nchunks; j0 += NF * 64) {
         Raw8<T> f[NF];
         int cnt[NF];
