@@ -155,11 +155,13 @@ def test_shift_mix_no_tokens(prior):
     check_shift(run_shift(case), case, f"shift-mix T=0 prior={prior}")
 
 
-@pytest.mark.parametrize("C", [20000, 20003])
-def test_shift_mix_wide_rows(C):
-    # rows longer than one pass of the statistics loop (256 lanes x 8 channels per wave pass)
-    case = wi.shift_mix_case(1, 5, C, seed=161, dtype="f32")
-    check_shift(run_shift(case), case, f"shift-mix wide C={C}")
+@pytest.mark.parametrize("dt,C", [("f32", 4096), ("f32", 20000), ("f32", 20003), ("f16", 8192), ("f16", 8200),
+                                  ("bf16", 9001)])
+def test_shift_mix_wide_rows(dt, C):
+    # the statistics hold a row of up to 4096 (fp32) or 8192 (2-byte) channels in registers;
+    # longer rows stream through in passes: both sides of the boundary, ragged ends
+    case = wi.shift_mix_case(1, 5, C, seed=161, dtype=dt)
+    check_shift(run_shift(case), case, f"shift-mix wide {dt} C={C}")
 
 
 def test_shift_mix_large_offset_and_constant_rows():
