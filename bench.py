@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "two_pass", "sequential"])
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bf16", action="store_true",
+                    help="bfloat16 in place of the workload's fp16 activations (inputs rounded from them)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the same-buffer (cache-warm) figure, e.g. under a profiler")
     ap.add_argument("--graph", action="store_true",
@@ -181,18 +183,29 @@ class Setup:
         stream = torch.cuda.current_stream(dev)
         hs = vp(stream.cuda_stream)
         self.stream = stream
-        tdt = {"f16": torch.float16, "f32": torch.float32}
+        # --bf16: every 2-byte activation (input and output) becomes bfloat16, the inputs rounded
+        # from the workload's fp16 values; fp32 tensors and the parameters stay as they are
+        act = torch.bfloat16 if args.bf16 else torch.float16
+        self.act = act
+        self.act_code = rw.RWKV_BF16 if args.bf16 else rw.RWKV_F16
+        tdt = {"f16": act, "f32": torch.float32}
         esz = {"f16": 2, "f32": 4}
         ei, eo = esz[wl.in_dtype], esz[wl.out_dtype]
-        self.io = f"{wl.in_dtype}->{wl.out_dtype}"
+        name16 = "bf16" if args.bf16 else "f16"
+        self.io = f"{wl.in_dtype}->{wl.out_dtype}".replace("f16", name16)
 
         def dev_t(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+        def dev_act(a):
+            # a device copy of an activation in the benchmark's 2-byte type (fp32 stays fp32)
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            return t.to(act) if t.dtype == torch.float16 else t
+
         opts = rw.Opts()
         opts.size = ctypes.sizeof(rw.Opts)
-        opts.in_dtype = rw.RWKV_F16 if wl.in_dtype == "f16" else rw.RWKV_F32
-        opts.out_dtype = rw.RWKV_F16 if wl.out_dtype == "f16" else rw.RWKV_F32
+        opts.in_dtype = self.act_code if wl.in_dtype == "f16" else rw.RWKV_F32
+        opts.out_dtype = self.act_code if wl.out_dtype == "f16" else rw.RWKV_F32
         opts.chunk_len = args.chunk_len
         opts.algo = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3}[args.algo]
         self.opts = opts
@@ -209,7 +222,7 @@ class Setup:
             self.launch_bytes = 4 * 2 * B * C + 2 * 12 * B * C + 8 * C
             calls = []
             for layer in case:
-                t = {n: dev_t(layer[n]) for n in ("k", "v", "r", "w", "u", "state")}
+                t = {n: dev_act(layer[n]) for n in ("k", "v", "r", "w", "u", "state")}
                 y = torch.empty((B, C), dtype=tdt[wl.out_dtype], device=dev)
                 self.keep.append((t, y))
                 calls.append((B, C, vp(t["w"].data_ptr()), vp(t["u"].data_ptr()), vp(t["k"].data_ptr()),
@@ -233,8 +246,8 @@ class Setup:
             # x, k, v read and y written once, x_prev read and x_last written, mix_r/k/v, w, u
             # (fp32 per channel; mix_k/v are read even when xk/xv are not requested), state out
             self.launch_bytes = 3 * ei * E + eo * E + 2 * ei * B * C + 5 * 4 * C + 3 * 4 * B * C
-            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in ("x", "k", "v")}
-            sh = {n: dev_t(case[n]) for n in ("x_prev", "mix_k", "mix_v", "mix_r", "w", "u")}
+            h = {n: dev_act(case[n]).cpu() for n in ("x", "k", "v")}
+            sh = {n: dev_act(case[n]) for n in ("x_prev", "mix_k", "mix_v", "mix_r", "w", "u")}
             self.keep.append(sh)
             set_bytes = (3 * ei + eo) * E
             R = max(2, math.ceil(args.rotate_gib * 2**30 / set_bytes))
@@ -258,7 +271,7 @@ class Setup:
             # k, v (and r) read, y written, w and u, the prior state read (if any), state out
             self.launch_bytes = ((len(names) * ei + eo) * E + 8 * C + (12 * B * C if wl.prior else 0)
                                  + 12 * B * C)
-            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in names}
+            h = {n: dev_act(case[n]).cpu() for n in names}
             sh = {n: dev_t(case[n]) for n in ("w", "u")}
             if wl.prior:
                 sh["state_in"] = dev_t(case["state_in"])
@@ -287,10 +300,11 @@ class Setup:
         """Buffers of the prologue (LayerNorm + token shift) and gate workloads."""
         B, T, C = self.B, self.T, self.C
         vp = ctypes.c_void_p
-        f16 = torch.float16
+        f16 = self.act  # the 2-byte activation type (fp16, or bfloat16 under --bf16)
 
         def dev_t(a):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            return t.to(f16) if t.dtype == torch.float16 else t
 
         if wl.kind == "shift":
             self.entry = "rwkv4_shift_mix"
@@ -298,7 +312,7 @@ class Setup:
             # x read, xk, xv, xr written (2 B each), x_prev read and x_last written, LayerNorm
             # weight and bias and three mixes (fp32 per channel)
             self.launch_bytes = 4 * 2 * E + 2 * 2 * B * C + 5 * 4 * C
-            hx = torch.from_numpy(np.ascontiguousarray(case["x"]))
+            hx = dev_t(case["x"]).cpu()
             sh = {n: dev_t(case[n]) for n in ("x_prev", "ln_weight", "ln_bias", "mix_k", "mix_v", "mix_r")}
             self.keep.append(sh)
             R = max(2, math.ceil(args.rotate_gib * 2**30 / (8 * E)))
@@ -312,13 +326,13 @@ class Setup:
                                    vp(sh["ln_bias"].data_ptr()), ctypes.c_float(case["ln_eps"]),
                                    vp(sh["mix_k"].data_ptr()), vp(sh["mix_v"].data_ptr()),
                                    vp(sh["mix_r"].data_ptr()), vp(s["xk"].data_ptr()), vp(s["xv"].data_ptr()),
-                                   vp(s["xr"].data_ptr()), rw.RWKV_F16, hs)])
+                                   vp(s["xr"].data_ptr()), self.act_code, hs)])
         else:
             self.entry = "rwkv4_channelmix_gate"
             self.fn = rw.lib.rwkv4_channelmix_gate
             # r, kv, residual read and y written, 2 B each
             self.launch_bytes = 4 * 2 * E
-            h = {n: torch.from_numpy(np.ascontiguousarray(case[n])) for n in ("r", "kv", "residual")}
+            h = {n: dev_t(case[n]).cpu() for n in ("r", "kv", "residual")}
             R = max(2, math.ceil(args.rotate_gib * 2**30 / (8 * E)))
             self.sets = []
             for _ in range(R):
@@ -326,7 +340,7 @@ class Setup:
                 s["y"] = torch.empty(E, dtype=f16, device=dev)
                 self.keep.append(s)
                 self.sets.append([(E, vp(s["r"].data_ptr()), vp(s["kv"].data_ptr()), vp(s["residual"].data_ptr()),
-                                   vp(s["y"].data_ptr()), rw.RWKV_F16, rw.RWKV_F16, hs)])
+                                   vp(s["y"].data_ptr()), self.act_code, self.act_code, hs)])
         self.cpu_case = case
         self.cpu_elements = E
         self.cpu_sample = f"the full workload B{B} T{T} C{C}"
