@@ -30,11 +30,19 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRowsPerBlock = 3;  // output rows per workgroup; its 4 waves take the statistics
-                                  // of these rows and of the row before them
-constexpr int kShiftThreads = 512;  // 8 waves: the first kRowsPerBlock + 1 take row statistics,
-                                    // all 8 write
-static_assert(kRowsPerBlock + 1 <= kShiftThreads / 64, "a wave per statistics row");
+constexpr int kRowsPerBlock = 4;     // output rows per workgroup; its first 5 waves take the
+                                     // statistics of these rows and of the row before them
+// Threads of a prologue workgroup: one per 8-channel chunk of a row (every thread then writes
+// one chunk of each row, with all of its loads in one batch), at least a wave per statistics
+// row, at most 1024 for 2-byte data and 512 for fp32 (whose chunks hold twice the registers;
+// wider rows loop).  Measured on the 14B shape (640 chunks): 4 rows x 640 threads 13.5 us,
+// against 3 rows x 512 threads (some threads taking two chunks) 13.9 us.
+template <typename T> constexpr int shift_max_threads() { return sizeof(T) == 4 ? 512 : 1024; }
+template <typename T> int shift_threads(int64_t C) {
+    const int64_t want = ((C + 7) / 8 + 63) / 64 * 64;
+    return (int)std::min<int64_t>(shift_max_threads<T>(), std::max<int64_t>(64 * (kRowsPerBlock + 1), want));
+}
+static_assert(64 * (kRowsPerBlock + 1) <= 512, "a wave per statistics row");
 
 template <typename T> struct Vec8;
 template <> struct Vec8<_Float16> { using type = h8; };
@@ -271,15 +279,15 @@ struct ShiftArgs {
     int vec;              // C % 8 == 0 and every pointer 16-byte aligned
 };
 
-// Workgroup (b, rows t0 .. t0+2), 8 waves.  Phase 1 (LayerNorm only): wave w < 4 takes the
-// statistics of row t0 - 1 + w (wave 0 of the first block takes row T - 1 instead, for x_last)
+// Workgroup (b, rows t0 .. t0+3), shift_threads<T>(C) threads.  Phase 1 (LayerNorm only): wave
+// w <= 4 takes the statistics of row t0 - 1 + w (wave 0 of the first block takes row T - 1 instead, for x_last)
 // and puts (mean, 1/sqrt(var + eps)) in LDS.  Phase 2: each thread takes 8-channel chunks; per
 // chunk it issues every load first (parameters, the previous row or x_prev, its rows, and the
 // last row for x_last), then normalises the rows in order, keeping the previous normalised row
 // in registers, and writes the mixes.  The first block of each batch row also writes x_last,
 // after it has read x_prev, so x_last may be x_prev itself.
 template <typename T, bool LN>
-__global__ void __launch_bounds__(kShiftThreads) shift_mix_kernel(ShiftArgs a) {
+__global__ void __launch_bounds__(shift_max_threads<T>()) shift_mix_kernel(ShiftArgs a) {
     __shared__ float s_mean[kRowsPerBlock + 1], s_rstd[kRowsPerBlock + 1];
     const int64_t nTB = std::max<int64_t>(1, (a.T + kRowsPerBlock - 1) / kRowsPerBlock);
     const int64_t b = blockIdx.x / nTB;
@@ -308,7 +316,7 @@ __global__ void __launch_bounds__(kShiftThreads) shift_mix_kernel(ShiftArgs a) {
     }
 
     const int64_t nchunks = (C + 7) / 8;
-    for (int64_t j = threadIdx.x; j < nchunks; j += kShiftThreads) {
+    for (int64_t j = threadIdx.x; j < nchunks; j += blockDim.x) {
         const int64_t c0 = 8 * j;
         const int cnt = (int)std::min<int64_t>(8, C - c0);
         // every load of the chunk first: one memory latency per chunk
@@ -423,9 +431,9 @@ hipError_t launch_shift_t(const ShiftArgs &a, hipStream_t s) {
     const int64_t nTB = std::max<int64_t>(1, (a.T + kRowsPerBlock - 1) / kRowsPerBlock);
     const dim3 grid((unsigned)(a.B * nTB));
     if (a.ln_w)
-        hipLaunchKernelGGL((shift_mix_kernel<T, true>), grid, dim3(kShiftThreads), 0, s, a);
+        hipLaunchKernelGGL((shift_mix_kernel<T, true>), grid, dim3(shift_threads<T>(a.C)), 0, s, a);
     else
-        hipLaunchKernelGGL((shift_mix_kernel<T, false>), grid, dim3(kShiftThreads), 0, s, a);
+        hipLaunchKernelGGL((shift_mix_kernel<T, false>), grid, dim3(shift_threads<T>(a.C)), 0, s, a);
     return hipGetLastError();
 }
 
