@@ -7,7 +7,8 @@ ragged last tiles, against the fp64 oracle element by element:
   * fp32 inputs on 64-token tiles;
   * the time mix with its xk/xv outputs.
 Also repeated calls on one caller workspace, which must give bitwise equal results (fixed fold
-order), and calls of different shapes on one workspace (the error word must stay put)."""
+order), calls of different shapes on one workspace (the error word must stay put), and two
+such calls running at once on two streams with their own workspaces."""
 import numpy as np
 import pytest
 
@@ -119,3 +120,37 @@ def test_multi_round_repeated_calls_one_workspace():
     check_state(host(outs[0][1]), ref, TOL["f16"], "multi-round repeated")
     for y, so in outs[1:]:
         assert t.equal(y, outs[0][0]) and t.equal(so, outs[0][1]), "multi-round calls differ"
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two chunked calls, each past one resident round and each with its own workspace, enqueued
+    on two streams with nothing ordering them: their workgroups share the GPU, and each call's
+    look-back only ever waits for its own earlier-dispatched tiles."""
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    cases = [wi.forward_case(1, 16000, 2048, seed=87, in_dtype="f16", gated=True, prior=True),
+             wi.forward_case(2, 9000, 1536, seed=88, in_dtype="f16", out_dtype="f32")]
+    for c in cases:
+        assert_past_one_round(c["B"], c["T"], c["C"], 128, 3 * 128 * 64 * 2)
+    refs = [oracle.forward(c) for c in cases]
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    dev_in, outs = [], []
+    for c in cases:
+        B, T, C = c["B"], c["T"], c["C"]
+        d = {n: to_dev(c.get(n), "f16" if n in ("k", "v", "r") else None) for n in ("k", "v", "r", "w", "u", "state_in")}
+        ws = t.zeros(rw.rwkv4_workspace_bytes(B, T, C, 128), dtype=t.uint8, device="cuda:0")
+        odt = t.float16 if c["out_dtype"] == "f16" else t.float32
+        y = t.full((B, T, C), float("nan"), dtype=odt, device="cuda:0")
+        so = t.full((3, B, C), float("nan"), device="cuda:0")
+        dev_in.append((d, ws)); outs.append((y, so))
+    t.cuda.synchronize()
+    note("concurrent forwards on two streams")
+    for c, (d, ws), (y, so), st in zip(cases, dev_in, outs, streams):
+        rw.rwkv4_wkv_forward(d["k"], d["v"], d["w"], d["u"], y=y, state_in=d["state_in"], state_out=so,
+                             r=d["r"], out_dtype=y.dtype, algo="chunked", chunk_len=128, workspace=ws,
+                             stream=st)
+    t.cuda.synchronize()
+    for c, ref, (y, so) in zip(cases, refs, outs):
+        what = f"concurrent B{c['B']} T{c['T']} C{c['C']}"
+        check_output(host(y), ref, TOL["f16"], what, out_dtype=c["out_dtype"])
+        check_state(host(so), ref, TOL["f16"], what)
