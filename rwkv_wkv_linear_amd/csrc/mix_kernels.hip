@@ -194,19 +194,23 @@ __device__ Moments row_moments(const T *row, int64_t C, bool vec, int lane) {
             cnt[m] = j < nchunks ? (int)std::min<int64_t>(8, C - 8 * j) : 0;
             if (cnt[m] > 0) f[m] = ldraw(row + 8 * j, vec, cnt[m]);
         }
+        // each value is scaled by 1/C as it is summed, so the sum is the mean itself and cannot
+        // overflow where the values do not
+        const float ic = 1.f / (float)C;
         float part[NF];
 #pragma unroll
         for (int m = 0; m < NF; ++m) {
             float a = 0.f;
             if (cnt[m] > 0)
-                a = ((f[m][0] + f[m][1]) + (f[m][2] + f[m][3])) + ((f[m][4] + f[m][5]) + (f[m][6] + f[m][7]));
+                a = ((f[m][0] * ic + f[m][1] * ic) + (f[m][2] * ic + f[m][3] * ic)) +
+                    ((f[m][4] * ic + f[m][5] * ic) + (f[m][6] * ic + f[m][7] * ic));
             part[m] = a;  // padding reads as 0
         }
 #pragma unroll
         for (int w = 1; w < NF; w *= 2)
 #pragma unroll
             for (int m = 0; m + w < NF; m += 2 * w) part[m] += part[m + w];
-        const float mean = wave_sum(part[0]) / (float)C;
+        const float mean = wave_sum(part[0]);
         if constexpr (sizeof(T) == 2) {
             // the packed values pass through an empty asm, so the second pass converts them
             // again instead of holding every converted value in registers across the passes
