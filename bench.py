@@ -286,7 +286,9 @@ class Setup:
                 sh["state_in"] = dev_t(case["state_in"])
             self.keep.append(sh)
             set_bytes = (len(names) * ei + eo) * E
-            R = max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
+            # one set of >= 1 GiB (four times the 256 MB Infinity Cache) is not cache-resident by
+            # itself and is not rotated (the long workload); smaller ones rotate to rotate_gib
+            R = 1 if set_bytes >= 2**30 else max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
             self.sets = []
             for _ in range(R):
                 s = {n: h[n].to(dev) for n in names}
