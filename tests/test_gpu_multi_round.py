@@ -2,7 +2,7 @@
 look-back runs over several rounds of workgroups (a tile's predecessors may already have
 retired, and anchor tiles carry the chain forward).  Each mode at a size past one round, with
 ragged last tiles, against the fp64 oracle element by element:
-  * gated with a prior state;
+  * gated with a prior state, in fp16 and in bfloat16;
   * ungated with fp32 output;
   * fp32 inputs on 64-token tiles;
   * the time mix with its xk/xv outputs.
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle
 import wkv_inputs as wi
-from gpu_util import TOL, check_output, check_state, host, note, to_dev, torch
+from gpu_util import TOL, check_output, check_state, host, note, to_dev, tol_for, torch
 
 LDS_PER_CU = 160 * 1024
 
@@ -33,7 +33,7 @@ def forward(case, chunk, out_dtype=None, workspace=None):
     import rwkv_wkv_linear_amd as rw
     t = torch()
     B, T, C = case["B"], case["T"], case["C"]
-    odt = {"f32": t.float32, "f16": t.float16}[out_dtype or case["out_dtype"]]
+    odt = {"f32": t.float32, "f16": t.float16, "bf16": t.bfloat16}[out_dtype or case["out_dtype"]]
     y = t.full((B, T, C), float("nan"), dtype=odt, device="cuda:0")
     so = t.full((3, B, C), float("nan"), device="cuda:0")
     note(f"multi-round forward B={B} T={T} C={C} in={case['in_dtype']} out={out_dtype or case['out_dtype']} "
@@ -53,6 +53,15 @@ def test_multi_round_gated_prior():
     y, so = forward(case, 128)
     check_output(host(y), ref, TOL["f16"], "multi-round gated", out_dtype="f16")
     check_state(host(so), ref, TOL["f16"], "multi-round gated")
+
+
+def test_multi_round_bf16_gated_prior():
+    case = wi.forward_case(2, 5000, 1024, seed=89, in_dtype="bf16", out_dtype="bf16", gated=True, prior=True)
+    assert_past_one_round(2, 5000, 1024, 128, 3 * 128 * 64 * 2)
+    ref = oracle.forward(case)
+    y, so = forward(case, 128)
+    check_output(host(y), ref, tol_for("bf16", "bf16"), "multi-round bf16", out_dtype="bf16")
+    check_state(host(so), ref, TOL["bf16"], "multi-round bf16")
 
 
 def test_multi_round_plain_fp32_out():
