@@ -122,6 +122,12 @@ typedef struct rwkv4_opts {
  * (RWKV_ALGO_CHUNKED) is not capturable into a HIP graph: its workspace is stamped per
  * launch from the host.  The sequential and two-pass algorithms are, given an explicit
  * opts->workspace (the library-cached one is allocated on first use).
+ * In the single-launch chunked scan a tile waits for the published states of earlier tiles
+ * of its chain, which were dispatched before it, so the wait ends even when other kernels
+ * share the GPU.  Each wait is still bounded (tens of milliseconds of polling): a wait that
+ * gives up, which only a broken precondition (such as a workspace shared with a concurrent
+ * call) can cause, writes NaN to its tile's outputs and makes later waits of the call give up
+ * at once, instead of hanging the GPU.
  */
 rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C,
                               const float *w, const float *u,
