@@ -126,8 +126,8 @@ typedef struct rwkv4_opts {
  * of its chain, which were dispatched before it, so the wait ends even when other kernels
  * share the GPU.  Each wait is still bounded (tens of milliseconds of polling): a wait that
  * gives up, which only a broken precondition (such as a workspace shared with a concurrent
- * call) can cause, writes NaN to its tile's outputs and makes later waits of the call give up
- * at once, instead of hanging the GPU.
+ * call) can cause, writes NaN to its tile's outputs and makes the call's later waits give up
+ * at once, instead of hanging the GPU; later calls on the workspace are unaffected.
  */
 rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C,
                               const float *w, const float *u,

@@ -40,7 +40,7 @@ struct ForwardArgs {
 struct ChunkWorkspace {
     uint64_t *words;  // single pass: [tiles][4][64] tagged words
     float *aggs;      // two passes: [tiles][64][4] tile aggregates
-    uint32_t *err;    // one word: set when a look-back wait gave up
+    uint32_t *err;    // one word: the epoch of a launch in which a look-back wait gave up
     uint32_t epoch;   // per-launch stamp; words of other launches never match
 };
 

@@ -347,10 +347,13 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
     while (!read_all()) {
         for (;;) {
             ++spins;
-            // give up after kMaxSpins, or at once when another wait has already given up
+            // give up after kMaxSpins, or at once when another wait of this launch has given up
+            // (the error word then holds the launch's epoch, so a failed launch leaves later
+            // launches on the same workspace unaffected)
             if (spins > kMaxSpins ||
-                ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-                atomicOr(ws.err, 1u);
+                ((spins & 63u) == 0 &&
+                 __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ws.epoch)) {
+                __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
             }
             __builtin_amdgcn_s_sleep(4);
