@@ -536,18 +536,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the wave's largest key (unknown until the last group lands): with the key spread of the wave
 // at most kGuardSpread every weight e^{k - mref} stays a normal fp32 number, and the guard is
 // decided after the last group exactly as in wave_summary.  Loads complete in issue order, so
-// when at most (instructions issued after group g) are outstanding, group g is in LDS.
-//
-// With a gate (MODE_GATED, MODE_TIMEMIX) it also forms every token's gate factor
-// G_i = 1 + e^{-r_i} (r_i = xr_i = mr x_i + (1 - mr) x_{i-1} for the time mix, in base 2 as
-// ga x_i + gb x_{i-1}; xprev is the token before the wave), which does not depend on the state.
-template <typename TIn, int NT, int L, int MODE, bool GATE>
-__device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, const TIn *gr, float ew, float uc,
-                                                  float ga, float gb, float xprev, float &mref, bool &fast,
-                                                  float (&Xs)[L], float (&Gs)[L]) {
+// when at most (instructions issued after group g) are outstanding, group g is in LDS: only
+// the k and v rows may be in flight when it is called.
+template <typename TIn, int L>
+__device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, float ew, float uc, float &mref,
+                                                  bool &fast, float (&Xs)[L]) {
     constexpr int CW = kTileChannels, G = 8, NG = L / G;
     constexpr int RPI = 64 / (CW / (16 / (int)sizeof(TIn)));  // rows per DMA instruction
-    constexpr int IPG = NT * (G / RPI);                       // DMA instructions per group
+    constexpr int IPG = 2 * (G / RPI);                        // DMA instructions per group (k, v)
     static_assert(L % G == 0 && G % RPI == 0, "groups are whole DMA instructions");
     float nn = 0.f, dd = 0.f, kmax = -INFINITY, kmin = INFINITY, m = 0.f;
 #pragma unroll
@@ -579,18 +575,6 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
             nn = fmaf(ew, nn, X * vb[i]);
             dd = fmaf(ew, dd, X);
         }
-        if constexpr (GATE && MODE == MODE_GATED) {
-#pragma unroll
-            for (int i = 0; i < G; ++i) Gs[g * G + i] = 1.f + __builtin_amdgcn_exp2f(-kLog2e * (float)gr[(g * G + i) * CW]);
-        }
-        if constexpr (GATE && MODE == MODE_TIMEMIX) {
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const float xx = (float)gr[(g * G + i) * CW];
-                Gs[g * G + i] = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xprev));
-                xprev = xx;
-            }
-        }
     }
     static_assert(NG <= 4, "at most four groups per wave");
     fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
@@ -606,11 +590,10 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
 // into registers before it is overwritten) and writes every finished batch of rows with
 // 16-byte stores (yrow 16-byte aligned, all 64 channels in range), MIX
 // writes the time-mix xk/xv rows.  Xs holds the weights e^{k_i - kmax} from the summary
-// phase; vr, gr point at the lane's first staged row.
-// With PRE the gate factors G_i = 1 + e^{-r_i} come precomputed in Gs (the summary phase
-// formed them while the rows were still landing) and the gate costs one multiply per token.
-template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX, bool PRE>
-__device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs)[L], const TIn *vr, const TIn *gr,
+// phase; vr, gr point at the lane's first staged row.  The gate factor is 1 + e^{-r_i}
+// (r_i = mr x_i + (1 - mr) x_{i-1} for the time mix, in base 2 as ga x_i + gb x_{i-1}).
+template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
+__device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, const TIn *gr,
                                           float eu, float ew, float ga, float gb, float mk, float mv, float &xs,
                                           float &nn, float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
                                           unsigned Cu, int lane) {
@@ -622,7 +605,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs
 #pragma unroll
     for (int h = 0; h < L; h += LB) {
         TIn vh[LB], gh[LB];
-        constexpr bool kNeedX = MODE != MODE_PLAIN && (!PRE || MIX);  // x (or r) rows still read here
+        constexpr bool kNeedX = MODE != MODE_PLAIN;  // x (or r) rows read here
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             vh[j] = vr[(h + j) * CW];
@@ -636,10 +619,9 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs
             const float num = fmaf(eu, P, nn);
             const float den = fmaf(eu, X, dd);
             float dg = den;  // den * (1 + e^{-r})
-            if constexpr (PRE && MODE != MODE_PLAIN) dg = den * Gs[i];
-            if constexpr (!PRE && MODE == MODE_GATED) dg = fmaf(den, __builtin_amdgcn_exp2f(-kLog2e * (float)gh[j]), den);
+            if constexpr (MODE == MODE_GATED) dg = fmaf(den, __builtin_amdgcn_exp2f(-kLog2e * (float)gh[j]), den);
             if constexpr (MODE == MODE_TIMEMIX) {
-                if constexpr (!PRE) dg = fmaf(den, __builtin_amdgcn_exp2f(fmaf(ga, (float)gh[j], gbx)), den);
+                dg = fmaf(den, __builtin_amdgcn_exp2f(fmaf(ga, (float)gh[j], gbx)), den);
                 if constexpr (MIX) {
                     const float xx = (float)gh[j];
                     const unsigned off = i * Cu + (unsigned)lane;
@@ -647,7 +629,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const float (&Gs
                     if (xvrow) st_stream(xvrow + off, (TIn)fmaf(mv, xx - xs, xs));
                     xs = xx;
                 }
-                if constexpr (!PRE) gbx = fmaf(gb, (float)gh[j], 0.f);
+                gbx = fmaf(gb, (float)gh[j], 0.f);
             }
             const TOut yv = (TOut)(num * rcp(dg));
             if constexpr (STAGE)
@@ -787,11 +769,12 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
     asm volatile("" ::: "memory");
 
-    // Phase A: stage this wave's rows.
-    {
-        const TIn *src[3] = {K, V, GR};
-        stage_rows<TIn, NT, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
-    }
+    // Phase A: stage this wave's k and v rows.  The r (or x) rows feed only the gate in the emit,
+    // so they are requested after the summary (phase B), behind the k and v rows of every
+    // workgroup, and land while the look-back runs: the summaries, and so the published
+    // aggregates, do not wait for a third of the bytes.
+    const TIn *src[3] = {K, V, GR};
+    stage_rows<TIn, 2, L>(src, rows, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs, a.vec16 != 0);
     const float ew = ex(wc), eu = ex(uc);
     // gate argument in base 2: -log2(e) * (mr x + (1 - mr) xs)
     const float ga = -kLog2e * mr, gb = -kLog2e * (1.f - mr);
@@ -818,20 +801,15 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
 
     // Phase B: summary of the wave's tokens from the empty state.  A full wave whose rows come
     // by 16-byte DMA takes them group by group as they land (wave-uniform choice); lanes past C
-    // then drop their summary (their rows are a copy of channel 0).
-    // 32-token waves with a receptance input also keep the gate factors 1 + e^{-r} of their
-    // tokens (formed during the summary, while rows are still landing, when staged).  The time
-    // mix forms its gate in the emit instead: its first token's r needs the previous wave's last
-    // row, which the summary phase may not wait for (measured slower when each wave fetched it).
-    constexpr bool PRE = L == 32 && MODE == MODE_GATED;
+    // then drop their summary (their rows are a copy of channel 0).  Then the wave requests its
+    // gate rows.
     float kmax;   // the weights' reference key: the largest key (or the first group's, staged)
     bool fast;
     float Xs[L];  // the weights e^{k_i - kmax} of a full wave on the fast path
-    float Gs[L];  // gate factors (PRE)
     St sum;
     const bool staged = a.vec16 && wlen == L;
     if (staged) {
-        sum = wave_summary_staged<TIn, NT, L, MODE, PRE>(kr, vr, gr, ew, uc, ga, gb, xs, kmax, fast, Xs, Gs);
+        sum = wave_summary_staged<TIn, L>(kr, vr, ew, uc, kmax, fast, Xs);
         if (!cok) {
             sum = st_empty();
             fast = false;
@@ -845,16 +823,10 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
         __builtin_amdgcn_wave_barrier();
         sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
-        if constexpr (PRE) {
-            float xp = xs;
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-                const float r = (float)gr[i * CW];
-                Gs[i] = 1.f + __builtin_amdgcn_exp2f(MODE == MODE_GATED ? -kLog2e * r : fmaf(ga, r, gb * xp));
-                xp = r;
-            }
-        }
     }
+    if constexpr (NT == 3)  // waited for before the emit
+        stage_rows<TIn, 1, L>(src + 2, rows + (size_t)2 * TW * CW, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs,
+                              a.vec16 != 0);
     sF[(0 * S + wv) * CW + lane] = sum.a;
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
@@ -906,6 +878,10 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
             }
         }
     }
+    if constexpr (NT == 3) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's gate rows have landed,
+        __syncthreads();                // and every other wave's (the time mix reads the previous wave's last x)
+    }
     if (PREFIX == PREFIX_LOOKBACK && wv == S - 1 && nTT > 1 && anchor && !last)
         publish(ws, chain + tt, kIncl, combine(prefix, agg, (float)tile_len, wc), lane);
     const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
@@ -935,7 +911,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
             TOut *yrow = Y + row0;
             TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
 #define RWKV_EMIT(STAGE, MIX)                                                                          \
-    emit_full<TIn, TOut, MODE, L, STAGE, MIX, PRE>(Xs, Gs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
+    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
                                                    xkrow, xvrow, ystage, Cu, lane)
             if constexpr (MODE == MODE_TIMEMIX) {
                 if (stage_y) {
