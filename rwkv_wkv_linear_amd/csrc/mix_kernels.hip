@@ -30,13 +30,11 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRowsPerBlock = 4;     // output rows per workgroup; its first 5 waves take the
-                                     // statistics of these rows and of the row before them
-// Threads of a prologue workgroup: one per 8-channel chunk of a row (every thread then writes
-// one chunk of each row, with all of its loads in one batch), at least a wave per statistics
-// row, at most 1024 for 2-byte data and 512 for fp32 (whose chunks hold twice the registers;
-// wider rows loop).  Measured on the 14B shape (640 chunks): 4 rows x 640 threads 13.5 us,
-// against 3 rows x 512 threads (some threads taking two chunks) 13.9 us.
+constexpr int kRowsPerBlock = 4;  // output rows per prologue workgroup (plus the row before them)
+// Rows of at most 1024 chunks of 8 take the single-read kernel (shift_mix_row_kernel, one
+// thread per chunk).  Wider rows take shift_mix_kernel with the threads below: one per chunk up
+// to 1024 for 2-byte data and 512 for fp32 (whose chunks hold twice the registers), the rest
+// looping, and at least a wave per statistics row.
 template <typename T> constexpr int shift_max_threads() { return sizeof(T) == 4 ? 512 : 1024; }
 template <typename T> int shift_threads(int64_t C) {
     const int64_t want = ((C + 7) / 8 + 63) / 64 * 64;
@@ -165,75 +163,35 @@ __device__ __forceinline__ Moments merge(const Moments &a, const Moments &b) {
     return Moments{n, fmaf(d, fb, a.mean), a.m2 + b.m2 + d * d * a.n * fb};
 }
 
-// Sum over the 64 lanes of a wave; every lane gets the same value (each pair adds the same two
-// numbers, and addition commutes).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+// Sum over the 64 lanes of a wave by cross-lane moves within each row of 16 lanes (DPP: swap
+// neighbours, swap pairs, mirror the half rows, mirror the row), after which every lane of a row
+// holds the row's sum; the four row sums are then read as scalars and added in a fixed order, so
+// every lane returns the same value.  No LDS round trips, unlike the butterfly of shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_rows(float v) {
+    v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);  // row_half_mirror
+    v += dpp_move<0x140>(v);  // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Moments of one row of C values, reduced over the 64 lanes of the calling wave; every lane
 // returns the row's result.
 template <typename T>
 __device__ Moments row_moments(const T *row, int64_t C, bool vec, int lane) {
-    // chunks in flight per lane: a whole row of up to 8192 (2-byte) or 4096 (fp32) channels is
-    // requested at once, so the pass costs one memory latency
+    // chunks in flight per lane: 8192 (2-byte) or 4096 (fp32) channels per pass
     constexpr int NF = sizeof(T) == 2 ? 16 : 8;
     const int64_t nchunks = (C + 7) / 8;
-    if (nchunks <= NF * 64) {
-        // The whole row is in registers: two passes over them, the sum (-> the mean), then the
-        // squared deviations from the mean, each a per-lane tree of chunk sums and a butterfly
-        // of plain adds.  This is the textbook two-pass variance (no E[x^2] - E[x]^2
-        // cancellation), with one division per row instead of one per chunk.
-        Raw8<T> f[NF];
-        int cnt[NF];
-#pragma unroll
-        for (int m = 0; m < NF; ++m) {
-            const int64_t j = m * 64 + lane;
-            cnt[m] = j < nchunks ? (int)std::min<int64_t>(8, C - 8 * j) : 0;
-            if (cnt[m] > 0) f[m] = ldraw(row + 8 * j, vec, cnt[m]);
-        }
-        // each value is scaled by 1/C as it is summed, so the sum is the mean itself and cannot
-        // overflow where the values do not
-        const float ic = 1.f / (float)C;
-        float part[NF];
-#pragma unroll
-        for (int m = 0; m < NF; ++m) {
-            float a = 0.f;
-            if (cnt[m] > 0)
-                a = ((f[m][0] * ic + f[m][1] * ic) + (f[m][2] * ic + f[m][3] * ic)) +
-                    ((f[m][4] * ic + f[m][5] * ic) + (f[m][6] * ic + f[m][7] * ic));
-            part[m] = a;  // padding reads as 0
-        }
-#pragma unroll
-        for (int w = 1; w < NF; w *= 2)
-#pragma unroll
-            for (int m = 0; m + w < NF; m += 2 * w) part[m] += part[m + w];
-        const float mean = wave_sum(part[0]);
-        if constexpr (sizeof(T) == 2) {
-            // the packed values pass through an empty asm, so the second pass converts them
-            // again instead of holding every converted value in registers across the passes
-#pragma unroll
-            for (int m = 0; m < NF; ++m) asm volatile("" : "+v"(f[m].v));
-        }
-#pragma unroll
-        for (int m = 0; m < NF; ++m) {
-            float q = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float d = f[m][i] - mean;
-                if (i < cnt[m]) q = fmaf(d, d, q);
-            }
-            part[m] = q;
-        }
-#pragma unroll
-        for (int w = 1; w < NF; w *= 2)
-#pragma unroll
-            for (int m = 0; m + w < NF; m += 2 * w) part[m] += part[m + w];
-        return Moments{(float)C, mean, wave_sum(part[0])};
-    }
-    // Longer rows stream through in passes of NF chunks, merged pairwise.
+    // The row streams through in passes of NF chunks per lane (every chunk's own mean and
+    // squared deviations, exact over its 8 values), merged pairwise.
     Moments acc{0.f, 0.f, 0.f};
     for (int64_t j0 = 0; j0 < nchunks; j0 += NF * 64) {
         Raw8<T> f[NF];
@@ -283,7 +241,7 @@ struct ShiftArgs {
     int vec;              // C % 8 == 0 and every pointer 16-byte aligned
 };
 
-// Workgroup (b, rows t0 .. t0+3), shift_threads<T>(C) threads.  Phase 1 (LayerNorm only): wave
+// Rows wider than 1024 chunks: workgroup (b, rows t0 .. t0+3), shift_threads<T>(C) threads.  Phase 1 (LayerNorm only): wave
 // w <= 4 takes the statistics of row t0 - 1 + w (wave 0 of the first block takes row T - 1 instead, for x_last)
 // and puts (mean, 1/sqrt(var + eps)) in LDS.  Phase 2: each thread takes 8-channel chunks; per
 // chunk it issues every load first (parameters, the previous row or x_prev, its rows, and the
@@ -397,6 +355,149 @@ __global__ void __launch_bounds__(shift_max_threads<T>()) shift_mix_kernel(Shift
     }
 }
 
+// Single-read form for rows of at most 1024 chunks of 8 (every thread holds one chunk of each
+// row): workgroup (b, rows t0 .. t0+3) with one thread per chunk.  Each thread loads its chunk
+// of five rows once (slot 0: the row before t0, or row T - 1 in the first block, which writes
+// x_last; slots 1..4: the block's rows), then the statistics run as a pipeline over the slots.
+// Stage k reduces the squared deviations of slot k - 1 (about its mean, from stage k - 1) and
+// the sum of slot k through one LDS exchange and one barrier, and then writes the outputs of
+// slot k - 1, so a row's outputs leave while the later rows are still landing.  The reductions
+// are the two-pass textbook ones: per-thread chunk sums, a butterfly of plain adds per wave,
+// then the wave partials added in wave order (every thread forms the same sums).
+template <typename T, bool LN>
+__global__ void __launch_bounds__(1024) shift_mix_row_kernel(ShiftArgs a) {
+    constexpr int R = kRowsPerBlock;
+    __shared__ float s_sum[R + 1][16], s_sq[R + 1][16];
+    const int64_t nTB = std::max<int64_t>(1, (a.T + R - 1) / R);
+    const int64_t b = blockIdx.x / nTB;
+    const int64_t t0 = (blockIdx.x - b * nTB) * R;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nW = blockDim.x >> 6;
+    const int64_t C = a.C;
+    const bool vec = a.vec != 0;
+    const T *X = static_cast<const T *>(a.x);
+    const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(R, a.T - t0));
+    const bool want_last = t0 == 0 && a.x_last != nullptr;
+    // slot 0: the row before t0, else (first block) the last row for x_last; block-uniform
+    const int64_t s0row = t0 > 0 ? t0 - 1 : (want_last && a.T > 0 ? a.T - 1 : -1);
+    auto slot_valid = [&](int k) { return k == 0 ? s0row >= 0 : k - 1 < rows; };
+
+    const int64_t nchunks = (C + 7) / 8;
+    const int64_t j = threadIdx.x;
+    const int64_t c0 = 8 * j;
+    const int cnt = j < nchunks ? (int)std::min<int64_t>(8, C - c0) : 0;
+    const T *col = X + b * a.T * C + c0;
+    // loads in the order they are needed: slot 0, x_prev, the parameters, then the rows
+    Raw8<T> xs[R + 1], xp;
+    float g[8], be[8], mx[3][8];
+    if (cnt > 0) {
+        if (s0row >= 0) xs[0] = ldraw(col + s0row * C, vec, cnt);
+        if (t0 == 0 && a.x_prev) xp = ldraw(static_cast<const T *>(a.x_prev) + b * C + c0, vec, cnt);
+        if constexpr (LN) {
+            ld8(a.ln_w + c0, vec, cnt, g);
+            if (a.ln_b)
+                ld8(a.ln_b + c0, vec, cnt, be);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) be[i] = 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+            if (a.mix[m]) ld8(a.mix[m] + c0, vec, cnt, mx[m]);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < rows) xs[r + 1] = ldraw<T, true>(col + (t0 + r) * C, vec, cnt);  // last reads
+    }
+
+    const float ic = 1.f / (float)C;
+    float mean[R + 1], rstd[R + 1], prev[8];
+#pragma unroll
+    for (int k = 0; k <= R + 1; ++k) {
+        if constexpr (LN) {
+            // stage k: squared deviations of slot k - 1 and the sum of slot k
+            const bool dq = k >= 1 && slot_valid(k - 1), dm = k <= R && slot_valid(k);
+            if (dq) {
+                float q = 0.f;
+                if (cnt > 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float d = xs[k - 1][i] - mean[k - 1];
+                        if (i < cnt) q = fmaf(d, d, q);
+                    }
+                }
+                q = wave_sum_rows(q);
+                if (lane == 0) s_sq[k - 1][wv] = q;
+            }
+            if (dm) {
+                float p = 0.f;  // padding reads as 0
+                if (cnt > 0) {
+                    const Raw8<T> &f = xs[k];
+                    p = ((f[0] * ic + f[1] * ic) + (f[2] * ic + f[3] * ic)) + ((f[4] * ic + f[5] * ic) + (f[6] * ic + f[7] * ic));
+                }
+                p = wave_sum_rows(p);
+                if (lane == 0) s_sum[k][wv] = p;
+            }
+            if (dq || dm) lds_barrier();  // the outputs of earlier slots stay in flight
+            if (dq) {
+                float v = 0.f;
+                for (int w = 0; w < nW; ++w) v += s_sq[k - 1][w];
+                rstd[k - 1] = 1.f / sqrtf(v / (float)C + a.eps);
+            }
+            if (dm) {
+                float m = 0.f;
+                for (int w = 0; w < nW; ++w) m += s_sum[k][w];
+                mean[k] = m;
+            }
+        }
+        if (k == 0 || cnt == 0) continue;
+        // outputs of slot k - 1
+        const int sl = k - 1;
+        auto norm = [&](const Raw8<T> &raw, float (&o)[8]) {
+            if constexpr (LN) {
+                const float mu = mean[sl], rs = rstd[sl];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = fmaf((raw[i] - mu) * rs, g[i], be[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = raw[i];
+            }
+        };
+        if (sl == 0) {
+            if (t0 > 0) {
+                norm(xs[0], prev);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) prev[i] = a.x_prev ? xp[i] : 0.f;
+                if (want_last) {
+                    // x_last: the normalised last row, or x_prev when there are no tokens (x_prev
+                    // was read above, so x_last may be x_prev itself)
+                    float last[8];
+                    if (a.T > 0) {
+                        norm(xs[0], last);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) last[i] = prev[i];
+                    }
+                    st8(static_cast<T *>(a.x_last) + b * C + c0, vec, cnt, last);
+                }
+            }
+        } else if (sl - 1 < rows) {
+            float cur[8];
+            norm(xs[sl], cur);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                if (a.mix[m]) {
+                    float o[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[i] = fmaf(mx[m][i], cur[i] - prev[i], prev[i]);
+                    st8(static_cast<T *>(a.out[m]) + (b * a.T + t0 + sl - 1) * C + c0, vec, cnt, o);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) prev[i] = cur[i];
+        }
+    }
+}
+
 struct GateArgs {
     int64_t n;
     const void *r, *kv, *res;
@@ -434,6 +535,16 @@ template <typename T>
 hipError_t launch_shift_t(const ShiftArgs &a, hipStream_t s) {
     const int64_t nTB = std::max<int64_t>(1, (a.T + kRowsPerBlock - 1) / kRowsPerBlock);
     const dim3 grid((unsigned)(a.B * nTB));
+    const int64_t nchunks = (a.C + 7) / 8;
+    if (nchunks <= 1024) {
+        // one thread per chunk, whole waves
+        const dim3 block((unsigned)std::max<int64_t>(64, (nchunks + 63) / 64 * 64));
+        if (a.ln_w)
+            hipLaunchKernelGGL((shift_mix_row_kernel<T, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((shift_mix_row_kernel<T, false>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
     if (a.ln_w)
         hipLaunchKernelGGL((shift_mix_kernel<T, true>), grid, dim3(shift_threads<T>(a.C)), 0, s, a);
     else

@@ -8,6 +8,19 @@
 
 namespace rwkvwkv {
 
+// Workgroup barrier for an exchange through LDS alone: each wave waits for its own LDS
+// accesses (lgkmcnt) and nothing else.  __syncthreads() also makes every global load and store
+// of the wave complete first (vmcnt(0)), which would stall on loads still streaming in;
+// global-to-LDS loads are not covered here, so a reader of another wave's staged rows needs
+// that wave to have waited for them (vmcnt) before the barrier.  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt(63) and expcnt(7) do not wait
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 enum Mode : int {
     MODE_PLAIN = 0,    // y = wkv
     MODE_GATED = 1,    // y = sigmoid(r) * wkv, r a [B,T,C] tensor

@@ -783,7 +783,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         sF[(1 * S + wv) * CW + lane] = part.b;
         sF[(2 * S + wv) * CW + lane] = part.k;
         sF[(3 * S + wv) * CW + lane] = part.n;
-        __syncthreads();
+        lds_barrier();
         for (int j = 0; j < S; ++j) {
             const int lj = j * q;
             if (lj < (int)tt) {
@@ -793,7 +793,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
                 prefix = (j == 0) ? pj : combine(prefix, pj, span, wc);
             }
         }
-        __syncthreads();  // the wave summaries reuse sF next
+        lds_barrier();  // the wave summaries reuse sF next
     }
     const TIn *kr = rows + ((size_t)0 * TW + wv * L) * CW + lane;
     const TIn *vr = rows + ((size_t)1 * TW + wv * L) * CW + lane;
@@ -831,7 +831,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     sF[(1 * S + wv) * CW + lane] = sum.b;
     sF[(2 * S + wv) * CW + lane] = sum.k;
     sF[(3 * S + wv) * CW + lane] = sum.n;
-    __syncthreads();
+    lds_barrier();  // not waiting for the gate rows in flight
 
     // Phase C: each wave folds the summaries of the waves before it (fixed order); the last
     // wave forms the tile aggregate and publishes it.
@@ -862,12 +862,12 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         q = (cnt + S - 1) / S;
         const int lo = a0 + wv * q, hi = std::min(lo + q, (int)tt);
         if (lo < hi) part = fold_published<kMaxAnchorGap / 4>(ws, chain, lo, hi, lo == a0, wc, (float)TW, lane);
-        __syncthreads();  // sI reuses sF: every wave has folded its summaries (phase C)
+        lds_barrier();  // sI reuses sF: every wave has folded its summaries (phase C)
         sI[(0 * S + wv) * CW + lane] = part.a;
         sI[(1 * S + wv) * CW + lane] = part.b;
         sI[(2 * S + wv) * CW + lane] = part.k;
         sI[(3 * S + wv) * CW + lane] = part.n;
-        __syncthreads();
+        lds_barrier();
         for (int j = 0; j < S; ++j) {
             const int lj = a0 + j * q;
             if (lj < (int)tt) {

@@ -155,11 +155,11 @@ def test_shift_mix_no_tokens(prior):
     check_shift(run_shift(case), case, f"shift-mix T=0 prior={prior}")
 
 
-@pytest.mark.parametrize("dt,C", [("f32", 4096), ("f32", 20000), ("f32", 20003), ("f16", 8192), ("f16", 8200),
-                                  ("bf16", 9001)])
+@pytest.mark.parametrize("dt,C", [("f32", 4096), ("f32", 8192), ("f32", 8200), ("f32", 20003), ("f16", 8192),
+                                  ("f16", 8200), ("bf16", 8191), ("bf16", 9001)])
 def test_shift_mix_wide_rows(dt, C):
-    # the statistics hold a row of up to 4096 (fp32) or 8192 (2-byte) channels in registers;
-    # longer rows stream through in passes: both sides of the boundary, ragged ends
+    # rows of up to 8192 channels are read once, a thread per 8-channel chunk; wider rows take
+    # their statistics in streamed passes merged pairwise: both sides of the boundary, ragged ends
     case = wi.shift_mix_case(1, 5, C, seed=161, dtype=dt)
     check_shift(run_shift(case), case, f"shift-mix wide {dt} C={C}")
 
