@@ -86,8 +86,24 @@ typedef enum rwkv_algo {
 } rwkv_algo;
 
 /*
+ * How a single-launch chunked scan's tiles hand their states to the later tiles of their chain
+ * (the workspace words of the look-back).  The GPU's eight XCDs each have their own L2, and
+ * workgroups are dispatched to them round-robin by index; with B * ceil(C / 64) a multiple of
+ * 8 and every workgroup resident at once, all tiles of a chain run on one XCD.
+ */
+typedef enum rwkv_publish {
+    RWKV_PUBLISH_AUTO = 0,           /* L2_FIRST when the layout above holds, else WRITE_THROUGH */
+    RWKV_PUBLISH_L2_FIRST = 1,       /* stored into the publishing XCD's L2 at once, where tiles
+                                        on the same XCD read it without a trip to memory, and
+                                        written through to memory after the tile's outputs: a
+                                        tile on another XCD still sees it, only later */
+    RWKV_PUBLISH_WRITE_THROUGH = 2   /* written through to memory at once */
+} rwkv_publish;
+
+/*
  * Options (all fields optional; pass NULL for: fp32 in and out, ungated, auto).
- * `size` must be set to sizeof(rwkv4_opts) (forward compatibility).
+ * `size` must be set to sizeof(rwkv4_opts) (forward compatibility); the size of the struct
+ * without its last field (`publish`, then taken as RWKV_PUBLISH_AUTO) is accepted too.
  */
 typedef struct rwkv4_opts {
     uint32_t size;
@@ -106,6 +122,8 @@ typedef struct rwkv4_opts {
                                 caller once before its first use (RWKV_ALGO_CHUNKED
                                 relies on it), then reusable */
     size_t workspace_bytes;
+    int32_t publish;         /* rwkv_publish (RWKV_ALGO_CHUNKED only; results are identical
+                                under every policy) */
 } rwkv4_opts;
 
 /*

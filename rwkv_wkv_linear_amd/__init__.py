@@ -22,6 +22,8 @@ RWKV_OK, RWKV_ERR_ARG, RWKV_ERR_DTYPE, RWKV_ERR_ALIGN, RWKV_ERR_HIP, RWKV_ERR_NO
 RWKV_F32, RWKV_F16, RWKV_BF16 = 0, 1, 2
 RWKV_ALGO_AUTO, RWKV_ALGO_SEQUENTIAL, RWKV_ALGO_CHUNKED, RWKV_ALGO_TWO_PASS = 0, 1, 2, 3
 _ALGOS = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3, 0: 0, 1: 1, 2: 2, 3: 3}
+RWKV_PUBLISH_AUTO, RWKV_PUBLISH_L2_FIRST, RWKV_PUBLISH_WRITE_THROUGH = 0, 1, 2
+_PUBLISH = {"auto": 0, "l2_first": 1, "write_through": 2, 0: 0, 1: 1, 2: 2}
 
 
 class Opts(ctypes.Structure):
@@ -35,6 +37,7 @@ class Opts(ctypes.Structure):
         ("algo", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("publish", ctypes.c_int32),
     ]
 
 
@@ -178,7 +181,7 @@ def _check(status):
         raise RwkvError(status, rwkv_last_error())
 
 
-def _opts(in_dtype, out_dtype, r=None, chunk_len=0, algo="auto", workspace=None):
+def _opts(in_dtype, out_dtype, r=None, chunk_len=0, algo="auto", workspace=None, publish="auto"):
     o = Opts()
     o.size = ctypes.sizeof(Opts)
     o.in_dtype = in_dtype
@@ -186,6 +189,7 @@ def _opts(in_dtype, out_dtype, r=None, chunk_len=0, algo="auto", workspace=None)
     o.r = _ptr(r)
     o.chunk_len = int(chunk_len)
     o.algo = _ALGOS[algo]
+    o.publish = _PUBLISH[publish]
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -193,7 +197,7 @@ def _opts(in_dtype, out_dtype, r=None, chunk_len=0, algo="auto", workspace=None)
 
 
 def rwkv4_wkv_forward(k, v, w, u, y=None, state_in=None, state_out=None, *, r=None, out_dtype=None,
-                      chunk_len=0, algo="auto", workspace=None, stream=None):
+                      chunk_len=0, algo="auto", workspace=None, publish="auto", stream=None):
     """y = WKV(k, v) (or sigmoid(r) * WKV when r is given); fills state_out if given.
     k, v, r: [B, T, C] float32/float16/bfloat16; w, u: [C] float32; states: [3, B, C] float32."""
     torch = _torch()
@@ -211,7 +215,7 @@ def rwkv4_wkv_forward(k, v, w, u, y=None, state_in=None, state_out=None, *, r=No
         y = torch.empty((B, T, C), dtype=odt, device=dev)
     _need(y, "y", (B, T, C), odt, dev)
     _need(workspace, "workspace", device=dev)
-    o = _opts(_dtype_code(k.dtype), _dtype_code(odt), r, chunk_len, algo, workspace)
+    o = _opts(_dtype_code(k.dtype), _dtype_code(odt), r, chunk_len, algo, workspace, publish)
     with torch.cuda.device(dev):
         _check(_get_lib().rwkv4_wkv_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                      _ptr(state_in), _ptr(state_out), _stream(stream, dev),
@@ -243,7 +247,7 @@ def rwkv4_wkv_step(k, v, r, w, u, state, y=None, *, out_dtype=None, stream=None)
 
 def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, xk_out=None,
                         xv_out=None, x_last=None, state_in=None, state_out=None, out_dtype=None,
-                        chunk_len=0, algo="auto", workspace=None, stream=None):
+                        chunk_len=0, algo="auto", workspace=None, publish="auto", stream=None):
     """Token shift + WKV + receptance gate: y = sigmoid(xr) * WKV(k, v).
     x, k, v [B, T, C]; x_prev, x_last [B, C] (x's dtype); mix_* [C] float32."""
     torch = _torch()
@@ -266,7 +270,7 @@ def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, x
         y = torch.empty((B, T, C), dtype=odt, device=dev)
     _need(y, "y", (B, T, C), odt, dev)
     _need(workspace, "workspace", device=dev)
-    o = _opts(_dtype_code(dt), _dtype_code(odt), None, chunk_len, algo, workspace)
+    o = _opts(_dtype_code(dt), _dtype_code(odt), None, chunk_len, algo, workspace, publish)
     with torch.cuda.device(dev):
         _check(_get_lib().rwkv4_timemix_fused(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(mix_k),
                                        _ptr(mix_v), _ptr(mix_r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),

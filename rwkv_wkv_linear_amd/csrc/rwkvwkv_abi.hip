@@ -103,11 +103,13 @@ struct Resolved {
     int32_t chunk_len = 0, algo = RWKV_ALGO_AUTO;
     void *workspace = nullptr;
     size_t workspace_bytes = 0;
+    int32_t publish = RWKV_PUBLISH_AUTO;
 };
 
 rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
     if (!o) return RWKV_OK;
-    if (o->size != sizeof(rwkv4_opts))
+    const bool has_publish = o->size == sizeof(rwkv4_opts);
+    if (!has_publish && o->size != offsetof(rwkv4_opts, publish))
         return fail(RWKV_ERR_ARG, "opts->size is %u, expected sizeof(rwkv4_opts) = %zu", o->size,
                     sizeof(rwkv4_opts));
     rwkv_status s;
@@ -121,6 +123,8 @@ rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
             return fail(RWKV_ERR_ARG, "opts->chunk_len %d: must be 0 or a power of two in [%d, %d]", c,
                         kMinChunk, kMaxChunk);
     }
+    if (has_publish && (o->publish < RWKV_PUBLISH_AUTO || o->publish > RWKV_PUBLISH_WRITE_THROUGH))
+        return fail(RWKV_ERR_ARG, "opts->publish %d is not a rwkv_publish", (int)o->publish);
     if (o->workspace && !aligned(o->workspace, 256))
         return fail(RWKV_ERR_ALIGN, "opts->workspace must be 256-byte aligned");
     r->in_dtype = o->in_dtype;
@@ -130,6 +134,7 @@ rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
     r->algo = o->algo;
     r->workspace = o->workspace;
     r->workspace_bytes = o->workspace_bytes;
+    r->publish = has_publish ? o->publish : RWKV_PUBLISH_AUTO;
     return RWKV_OK;
 }
 
@@ -163,6 +168,7 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
 
     a.in_dt = o.in_dtype;
     a.out_dt = o.out_dtype;
+    a.publish = o.publish;
     bool vec = (C % 4) == 0;
     for (const void *p : ins)
         if (p && !aligned(p, 4 * ei)) vec = false;

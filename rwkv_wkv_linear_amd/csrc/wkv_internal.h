@@ -41,6 +41,7 @@ struct ForwardArgs {
     float *state_out;       // may be null
     int in_dt, out_dt;  // rwkv_dtype codes: 0 fp32, 1 fp16, 2 bf16
     int mode;
+    int publish;  // rwkv_publish: how look-back states are published (single-pass chunked scan)
     int vec;    // 1: C % 4 == 0 and activation pointers aligned for 4-element vectors
     int vec16;   // 1: input rows split into 16-byte chunks (C % (16 / size) == 0, 16-B aligned)
     int vec16y;  // 1: the same for y

@@ -36,6 +36,7 @@
 //                     HBM traffic is one read of each input and one write of y.
 //   wkv_passthrough   T = 0: copy the state (and x_prev to x_last).
 
+#include "rwkvwkv.h"
 #include "wkv_internal.h"
 
 #include <algorithm>
@@ -298,15 +299,26 @@ __global__ void __launch_bounds__(256) wkv_seq_kernel(ForwardArgs a) {
 // as relaxed agent-scope 64-bit atomics.  A reader accepts a tile's state when all four of
 // its words carry the expected tag, so no fence (and no L2 write-back or invalidate) is
 // needed: each word is self-validating and the fields need no mutual order.
+// With local set the words are stored at workgroup scope: they stay in this XCD's L2, where the
+// device-scope loads of a reader on the same XCD find them without a trip to memory (a reader
+// on another XCD cannot see them until they are stored again at device scope).  Otherwise they
+// are written through to memory at once.
 __device__ __forceinline__ void publish(const ChunkWorkspace &ws, int64_t tile, uint32_t kind,
-                                        const St &s, int ch) {
+                                        const St &s, int ch, bool local) {
     uint64_t *dst = ws.words + tile * (4 * kTileChannels);
     const uint64_t tag = (uint64_t)((ws.epoch << 2) | kind) << 32;
     const float f[4] = {s.a, s.b, s.k, s.n};
+    if (local) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        __hip_atomic_store(dst + m * kTileChannels + ch, tag | __float_as_uint(f[m]), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        for (int m = 0; m < 4; ++m)
+            __hip_atomic_store(dst + m * kTileChannels + ch, tag | __float_as_uint(f[m]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            __hip_atomic_store(dst + m * kTileChannels + ch, tag | __float_as_uint(f[m]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // Fold of the published states of tiles [lo, hi) of a chain, left to right; tile lo is an
@@ -677,7 +689,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 // call is resident at once.
 template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
 __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorkspace &ws, int S, int nCT, int nTT,
-                                          int TW, int M, int rot) {
+                                          int TW, int M, int rot, int lp) {
     constexpr int CW = kTileChannels;
     constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -847,7 +859,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     if constexpr (PREFIX == PREFIX_LOOKBACK) {
         if (wv == S - 1) {
             agg = combine(excl, sum, (float)wlen, wc);
-            if (nTT > 1 && !anchor && !last) publish(ws, chain + tt, kAgg, agg, lane);
+            if (nTT > 1 && !anchor && !last) publish(ws, chain + tt, kAgg, agg, lane, lp != 0);
         }
     }
 
@@ -878,12 +890,15 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
             }
         }
     }
+    // an anchor's inclusive state does not wait for the gate rows: the chain's later tiles fold it
+    if (PREFIX == PREFIX_LOOKBACK && wv == S - 1 && nTT > 1 && anchor && !last) {
+        agg = combine(prefix, agg, (float)tile_len, wc);  // from here on the published (inclusive) state
+        publish(ws, chain + tt, kIncl, agg, lane, lp != 0);
+    }
     if constexpr (NT == 3) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's gate rows have landed,
         __syncthreads();                // and every other wave's (the time mix reads the previous wave's last x)
     }
-    if (PREFIX == PREFIX_LOOKBACK && wv == S - 1 && nTT > 1 && anchor && !last)
-        publish(ws, chain + tt, kIncl, combine(prefix, agg, (float)tile_len, wc), lane);
     const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
 
     // Phase E: emit y for the wave's tokens, starting from st.
@@ -979,6 +994,11 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         fin = s2;
     }
 
+    // A state published into this XCD's L2 is now written through for readers on other XCDs
+    // (the outputs above are out of the way).
+    if (PREFIX == PREFIX_LOOKBACK && lp && wv == S - 1 && nTT > 1 && !last)
+        publish(ws, chain + tt, anchor ? kIncl : kAgg, agg, lane, false);
+
     // Phase F: the lane holding token T-1 writes the final state (and x_last).
     if (nval > 0 && t0 + nval == a.T) {
         if (a.state_out) {
@@ -996,8 +1016,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
 // share a CU.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
-    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot) {
-    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot);
+    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp) {
+    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp);
 }
 
 // 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
@@ -1005,8 +1025,8 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
 // occupancy each wave may hold its 32 weights in registers.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(256)
-    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot) {
-    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot);
+    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp) {
+    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1157,12 +1177,18 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
                                : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
     const int64_t slots = resident_slots(kern, 64 * S, lds);
     const int rot = (slots > 0 && blocks > slots) ? 1 : 0;  // more than one round of workgroups
+    // States go into the publishing XCD's L2 first when every tile of a chain runs on one XCD:
+    // workgroup i runs on XCD i mod 8, tile (tt, chain r) is workgroup tt * B * nCT + r, so
+    // without the per-tile rotation that holds when B * nCT is a multiple of 8.
+    const bool one_xcd = rot == 0 && (a.B * nCT) % 8 == 0;
+    const int lp = PREFIX == PREFIX_LOOKBACK && (a.publish == RWKV_PUBLISH_L2_FIRST ||
+                                                 (a.publish == RWKV_PUBLISH_AUTO && one_xcd));
     if constexpr (L == 32)
         hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M, rot);
+                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp);
     else
         hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M, rot);
+                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp);
     return hipGetLastError();
 }
 

@@ -84,6 +84,16 @@ def test_bad_opts():
     for c in (32, 100, 2048, -64):
         assert fwd(o=opts(chunk_len=c)) == rw.RWKV_ERR_ARG, c
     assert fwd(o=opts(workspace=P + 4, workspace_bytes=1 << 20)) == rw.RWKV_ERR_ALIGN
+    for bad in (-1, 3):
+        assert fwd(o=opts(publish=bad)) == rw.RWKV_ERR_ARG and "opts->publish" in rw.rwkv_last_error()
+
+
+def test_opts_without_publish_field_accepted():
+    # the struct as it was before its last field: the size check passes (publish is AUTO), so
+    # the call goes on to fail at the next check, the bad dtype
+    o = opts(in_dtype=7)
+    o.size = rw.Opts.publish.offset
+    assert fwd(o=o) == rw.RWKV_ERR_DTYPE
 
 
 def test_chunk_len_beyond_mode_limit():
