@@ -88,11 +88,14 @@ typedef enum rwkv_algo {
 /*
  * How a single-launch chunked scan's tiles hand their states to the later tiles of their chain
  * (the workspace words of the look-back).  The GPU's eight XCDs each have their own L2, and
- * workgroups are dispatched to them round-robin by index; with B * ceil(C / 64) a multiple of
- * 8 and every workgroup resident at once, all tiles of a chain run on one XCD.
+ * workgroups are dispatched to them round-robin by index.  When every workgroup is resident at
+ * once and the workgroups of a time tile number a multiple of 8 (B * ceil(C / 64) chains, padded
+ * with workgroups that return at once when that adds at most half again), all tiles of a chain
+ * run on one XCD.
  */
 typedef enum rwkv_publish {
-    RWKV_PUBLISH_AUTO = 0,           /* L2_FIRST when the layout above holds, else WRITE_THROUGH */
+    RWKV_PUBLISH_AUTO = 0,           /* L2_FIRST when the layout above holds (padding included),
+                                        else WRITE_THROUGH */
     RWKV_PUBLISH_L2_FIRST = 1,       /* stored into the publishing XCD's L2 at once, where tiles
                                         on the same XCD read it without a trip to memory, and
                                         written through to memory after the tile's outputs: a

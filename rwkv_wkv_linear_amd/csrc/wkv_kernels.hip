@@ -689,7 +689,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 // call is resident at once.
 template <typename TIn, typename TOut, int MODE, int L, int PREFIX>
 __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorkspace &ws, int S, int nCT, int nTT,
-                                          int TW, int M, int rot, int lp) {
+                                          int TW, int M, int rot, int lp, int G) {
     constexpr int CW = kTileChannels;
     constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -701,8 +701,9 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     // wave-uniform row and tile addresses in SGPRs
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t BCT = a.B * nCT;
-    const int64_t tt = blockIdx.x / BCT;
-    const int64_t rem = blockIdx.x - tt * BCT;
+    const int64_t tt = blockIdx.x / G;  // G workgroups per time tile: the BCT chains, then padding
+    const int64_t rem = blockIdx.x - tt * G;
+    if (rem >= BCT) return;
     int64_t b, ct;
     tile_chain(rem, tt, rot, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
@@ -1016,8 +1017,8 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
 // share a CU.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
-    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp) {
-    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp);
+    wkv_tile_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp, int G) {
+    tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
 }
 
 // 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
@@ -1025,8 +1026,8 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
 // occupancy each wave may hold its 32 weights in registers.
 template <typename TIn, typename TOut, int MODE, int PREFIX>
 __global__ void __launch_bounds__(256)
-    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp) {
-    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp);
+    wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp, int G) {
+    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1176,19 +1177,26 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     const void *kern = L == 32 ? reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>)
                                : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
     const int64_t slots = resident_slots(kern, 64 * S, lds);
-    const int rot = (slots > 0 && blocks > slots) ? 1 : 0;  // more than one round of workgroups
     // States go into the publishing XCD's L2 first when every tile of a chain runs on one XCD:
-    // workgroup i runs on XCD i mod 8, tile (tt, chain r) is workgroup tt * B * nCT + r, so
-    // without the per-tile rotation that holds when B * nCT is a multiple of 8.
-    const bool one_xcd = rot == 0 && (a.B * nCT) % 8 == 0;
+    // workgroup i runs on XCD i mod 8, tile (tt, chain r) is workgroup tt * G + r with G
+    // workgroups per time tile, so without the per-tile rotation that holds when G is a
+    // multiple of 8.  G is B * nCT, padded to a multiple of 8 with workgroups that return at
+    // once when the padded grid still fits in one round and adds at most half again.
+    const int64_t BCT = a.B * (int64_t)nCT, Gp = (BCT + 7) / 8 * 8;
+    const bool pad = PREFIX == PREFIX_LOOKBACK && nTT > 1 && a.publish != RWKV_PUBLISH_WRITE_THROUGH &&
+                     Gp != BCT && slots > 0 && Gp * nTT <= slots && 2 * Gp <= 3 * BCT;
+    const int64_t G = pad ? Gp : BCT;
+    const int64_t grid = G * nTT;
+    const int rot = (slots > 0 && grid > slots) ? 1 : 0;  // more than one round of workgroups
+    const bool one_xcd = rot == 0 && G % 8 == 0;
     const int lp = PREFIX == PREFIX_LOOKBACK && (a.publish == RWKV_PUBLISH_L2_FIRST ||
                                                  (a.publish == RWKV_PUBLISH_AUTO && one_xcd));
     if constexpr (L == 32)
-        hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp);
+        hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
+                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
     else
-        hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)blocks), dim3(64 * S), lds, s,
-                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp);
+        hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
+                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
     return hipGetLastError();
 }
 
