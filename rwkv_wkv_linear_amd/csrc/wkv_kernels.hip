@@ -53,7 +53,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyP = -1.0e38f;  // p of the empty state (finite, so differences stay defined)
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
-constexpr uint32_t kMaxSpins = 1u << 18;  // ~30 ms of polling before a look-back gives up
+constexpr uint32_t kMaxSpins = 1u << 16;  // tens of milliseconds of polling (one memory round trip per spin) before a look-back gives up
 constexpr int kMaxAnchorGap = 16;         // spacing of anchor tiles in a chain (S >= 4 waves poll <= 4 each)
 
 template <typename T> struct Raw;
@@ -335,10 +335,9 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
     const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
     uint64_t w[MAXT][4];
     const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
-    // One attempt reads every word.  The predecessors have usually published by the time a
-    // tile gets here, so the first attempt normally succeeds in a single memory round trip;
-    // otherwise a cheap probe (one word per tile) spins until all look ready, and the full
-    // read repeats.
+    // Every attempt reads every word, back to back until all carry the expected tags: a state
+    // found in the same XCD's L2 costs one short round trip, so a separate probe followed by a
+    // second full read would only add one.
     auto read_all = [&]() -> bool {
         bool all = true;
 #pragma unroll
@@ -357,25 +356,14 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
     };
     uint32_t spins = 0;
     while (!read_all()) {
-        for (;;) {
-            ++spins;
-            // give up after kMaxSpins, or at once when another wait of this launch has given up
-            // (the error word then holds the launch's epoch, so a failed launch leaves later
-            // launches on the same workspace unaffected)
-            if (spins > kMaxSpins ||
-                ((spins & 63u) == 0 &&
-                 __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ws.epoch)) {
-                __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
-            }
-            __builtin_amdgcn_s_sleep(4);
-            bool probe = true;
-            if (ch < cnt) {
-                const uint64_t x = __hip_atomic_load(tiles + ch * (4 * kTileChannels) + 3 * kTileChannels,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                probe = (uint32_t)(x >> 32) == ((ch == 0 && lo_incl) ? want_incl : want_agg);
-            }
-            if (__all(probe)) break;
+        ++spins;
+        // give up after kMaxSpins, or at once when another wait of this launch has given up (the
+        // error word then holds the launch's epoch, so a failed launch leaves later launches on
+        // the same workspace unaffected)
+        if (spins > kMaxSpins ||
+            ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ws.epoch)) {
+            __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
         }
     }
     St acc = st_empty();
