@@ -692,6 +692,10 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const int64_t tt = blockIdx.x / G;  // G workgroups per time tile: the BCT chains, then padding
     const int64_t rem = blockIdx.x - tt * G;
     if (rem >= BCT) return;
+    // Until its emit a wave runs at raised issue priority: its summary and publish are on the
+    // critical path of the chain's later tiles, while the emit of a tile whose prefix has arrived
+    // is not, and at the end of a launch the two compete for the same SIMDs.
+    __builtin_amdgcn_s_setprio(2);
     int64_t b, ct;
     tile_chain(rem, tt, rot, BCT, nCT, b, ct);
     const int64_t c = ct * CW + lane;
@@ -891,6 +895,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
 
     // Phase E: emit y for the wave's tokens, starting from st.
+    __builtin_amdgcn_s_setprio(0);
     TOut *Y = static_cast<TOut *>(a.y);
     TIn *XKO = static_cast<TIn *>(a.xk_out);
     TIn *XVO = static_cast<TIn *>(a.xv_out);
