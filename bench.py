@@ -117,15 +117,16 @@ def counters_traffic():
 
 def cpu_baseline(name, case, elements, sample):
     """The fp64 oracle as it stands, on the host cores: median of repeated runs over `case`
-    (at least 3, about CPU_BUDGET_S seconds in all), and for the C oracle (OpenMP over the
-    channels) also one run on a single thread."""
+    (at least 3, about CPU_BUDGET_S seconds in all), then one run on a single thread.  Every
+    oracle routine is C with OpenMP over independent lanes (channels, or rows and elements for
+    the mixers); numpy only marshals the arrays and, for the prologue, runs the token shift's
+    elementwise mix."""
     import oracle
-    numpy_oracle = name in ("lnshift14b", "cmgate14b")  # numpy elementwise work: one thread
     run = {"timemix14b": oracle.timemix, "decode14b": lambda c: [oracle.step(l) for l in c],
            "lnshift14b": oracle.shift_mix,
            "cmgate14b": lambda c: oracle.receptance_gate(c["r"], c["kv"], c["residual"])}.get(
         name, oracle.forward)
-    threads = 1 if numpy_oracle else oracle.num_threads()
+    threads = oracle.num_threads()
     times = []
     t_end = time.perf_counter() + CPU_BUDGET_S
     while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
@@ -138,17 +139,26 @@ def cpu_baseline(name, case, elements, sample):
         "unit": "tokens\u00b7channels/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{sample}; fp64 " + ("numpy oracle" if numpy_oracle else "C oracle with OpenMP over channels")
-                  + f", median of {len(times)} runs",
+        "sample": f"{sample}; fp64 C oracle with OpenMP on {threads} threads, median of {len(times)} runs",
     }
-    if not numpy_oracle and threads > 1:
+    if threads > 1:
         # one run on one thread (the last oracle work of the process)
         one = {"timemix14b": lambda c: oracle.timemix(c, nthreads=1),
-               "decode14b": lambda c: [oracle.step(l, nthreads=1) for l in c]}.get(
-            name, lambda c: oracle.forward(c, nthreads=1))
+               "decode14b": lambda c: [oracle.step(l, nthreads=1) for l in c]}.get(name)
+        if one is None and name in ("lnshift14b", "cmgate14b"):
+            prev = oracle.num_threads()
+            oracle.set_threads(1)
+            one = lambda c: run(c)  # noqa: E731
+        elif one is None:
+            prev = None
+            one = lambda c: oracle.forward(c, nthreads=1)  # noqa: E731
+        else:
+            prev = None
         t0 = time.perf_counter()
         one(case)
         out["value_one_thread"] = elements / (time.perf_counter() - t0)
+        if prev is not None:
+            oracle.set_threads(prev)
     return out
 
 def copy_kernel(args):
@@ -474,6 +484,10 @@ def main():
                                        "launches": Kw}
     result["cpu_baseline"] = None if args.no_cpu_baseline else \
         cpu_baseline(name, su.cpu_case, su.cpu_elements, su.cpu_sample)
+    if result["cpu_baseline"]:
+        # the GPU's throughput over the oracle's on all host threads (context: the oracle is a
+        # plain fp64 reference, never tuned)
+        result["gpu_over_cpu_baseline"] = result["value"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
 
 

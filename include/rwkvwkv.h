@@ -119,7 +119,8 @@ typedef struct rwkv4_opts {
                                 128 (2-byte) / 64 (fp32): the tile's rows are staged in
                                 the workgroup's LDS */
     int32_t algo;            /* rwkv_algo */
-    void *workspace;         /* chunked scan scratch: NULL = library-cached per device;
+    void *workspace;         /* chunked scan scratch: NULL = library-cached per (device,
+                                stream), allocated on first use;
                                 else device memory of workspace_bytes >= the size
                                 rwkv4_workspace_bytes() reports, zero-filled by the
                                 caller once before its first use (RWKV_ALGO_CHUNKED
@@ -138,17 +139,24 @@ typedef struct rwkv4_opts {
  *   state_in     [3,B,C] fp32 prior state, or NULL for the empty state.
  *   state_out    [3,B,C] fp32 state after the T tokens, or NULL.  May equal
  *                state_in exactly (in-place update); no other overlap is allowed.
- * Concurrent calls on different streams that use a chunked scan must not share
- * a workspace (pass opts->workspace).  The single-launch chunked scan
- * (RWKV_ALGO_CHUNKED) is not capturable into a HIP graph: its workspace is stamped per
- * launch from the host.  The sequential and two-pass algorithms are, given an explicit
- * opts->workspace (the library-cached one is allocated on first use).
+ * Workspace.  A chunked scan over more than one tile per chain needs scratch memory: the
+ * caller's (opts->workspace) or, when that is NULL, a workspace the library allocates on first
+ * use and keeps per (device, stream) until the process ends.  Calls on one stream may share a
+ * workspace; calls that may run at the same time (different streams) must not, so a caller
+ * that passes one workspace to several streams must serialise them itself.
+ * Graph capture.  The single-launch chunked scan stamps its workspace per launch from the
+ * host, so it cannot be replayed from a graph: on a capturing stream AUTO takes the two-pass
+ * scan, which needs opts->workspace (RWKV_ERR_ARG without it), and RWKV_ALGO_CHUNKED is
+ * refused with RWKV_ERR_ARG.  The sequential algorithm, and any call whose T fits in one tile,
+ * capture as they are.
  * In the single-launch chunked scan a tile waits for the published states of earlier tiles
  * of its chain, which were dispatched before it, so the wait ends even when other kernels
  * share the GPU.  Each wait is still bounded (tens of milliseconds of polling): a wait that
  * gives up, which only a broken precondition (such as a workspace shared with a concurrent
- * call) can cause, writes NaN to its tile's outputs and makes the call's later waits give up
- * at once, instead of hanging the GPU; later calls on the workspace are unaffected.
+ * call) can cause, writes NaN to its tile's outputs and sets the workspace's error word
+ * instead of hanging the GPU.  While that word is set, every look-back on the workspace gives
+ * up at once (its tiles' outputs are NaN), in the same call and in later ones, until
+ * rwkv4_lookback_status reads and clears it.
  */
 rwkv_status rwkv4_wkv_forward(int64_t B, int64_t T, int64_t C,
                               const float *w, const float *u,
@@ -225,6 +233,24 @@ rwkv_status rwkv4_shift_mix(int64_t B, int64_t T, int64_t C,
 rwkv_status rwkv4_channelmix_gate(int64_t n, const void *r, const void *kv, const void *residual,
                                   void *y, rwkv_dtype in_dtype, rwkv_dtype out_dtype,
                                   hipStream_t stream);
+
+/*
+ * Whether a look-back wait of a single-launch chunked scan on a workspace gave up since the
+ * workspace was zero-filled or last checked (the scans' outputs from then on hold NaN in every
+ * tile that waited).  Safe to call at any time: it synchronises `stream` first, so the work
+ * enqueued on it has finished, then reads the workspace's error word into *gave_up (1 set,
+ * 0 clear) and clears it, so later calls on the workspace run normally again.
+ *   workspace    the caller's workspace (opts->workspace of the calls), or NULL for the
+ *                library-cached workspace of the current device and `stream` (*gave_up = 0
+ *                when none exists yet).  The error word is the first 4 bytes of a workspace:
+ *                a caller can set it to any nonzero value to make the next calls' look-backs
+ *                give up at once, which exercises its own failure handling.
+ *   stream       the stream whose work is waited for (and, with workspace NULL, whose cached
+ *                workspace is read).
+ * Returns RWKV_ERR_ARG for a NULL gave_up, RWKV_ERR_ALIGN for a workspace that is not 256-byte
+ * aligned, RWKV_ERR_HIP if the synchronisation or the copy fails.
+ */
+rwkv_status rwkv4_lookback_status(void *workspace, hipStream_t stream, int32_t *gave_up);
 
 /* Static text for a status code. */
 const char *rwkv_status_string(rwkv_status s);

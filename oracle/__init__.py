@@ -77,6 +77,8 @@ def _load():
             lib.oracle_receptance_gate.argtypes = [_i64, _dp, _dp, _dp, _dp]
             lib.oracle_receptance_gate.restype = None
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -108,6 +110,11 @@ def _restore_library(handle):
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the routines that take no thread count (layer_norm, receptance_gate)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _f64(a):

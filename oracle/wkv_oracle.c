@@ -66,6 +66,9 @@ static void set_threads(int nthreads)
 #endif
 }
 
+/* Threads of the routines that take no thread count (LayerNorm, the gate); 0 leaves it. */
+void oracle_set_num_threads(int nthreads) { set_threads(nthreads); }
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

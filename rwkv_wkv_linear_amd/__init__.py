@@ -78,6 +78,8 @@ def _load():
     lib.rwkv_last_error.restype = ctypes.c_char_p
     lib.rwkv4_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int32]
     lib.rwkv4_workspace_bytes.restype = ctypes.c_size_t
+    lib.rwkv4_lookback_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.rwkv4_lookback_status.restype = ctypes.c_int
     lib.rwkv_abi_version.argtypes = []
     lib.rwkv_abi_version.restype = ctypes.c_int
     return lib
@@ -279,6 +281,20 @@ def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, x
     return y
 
 
+def rwkv4_lookback_status(workspace=None, *, stream=None, device=None):
+    """True when a look-back wait of a single-launch chunked scan on `workspace` (a tensor passed
+    as the calls' workspace; None: the library-cached workspace of `stream`, by default the
+    current stream of `device`) gave up since it was last checked; clears the flag.  Waits for
+    the stream's work first."""
+    torch = _torch()
+    dev = workspace.device if workspace is not None else (device or torch.device("cuda", torch.cuda.current_device()))
+    _need(workspace, "workspace", device=dev)
+    flag = ctypes.c_int32(0)
+    with torch.cuda.device(dev):
+        _check(_get_lib().rwkv4_lookback_status(_ptr(workspace), _stream(stream, dev), ctypes.byref(flag)))
+    return bool(flag.value)
+
+
 def rwkv4_shift_mix(x, x_prev=None, *, ln_weight=None, ln_bias=None, ln_eps=1e-5, mix_k=None, mix_v=None,
                     mix_r=None, xk=None, xv=None, xr=None, x_last=None, stream=None):
     """Pre-LN token-shift prologue: n = LayerNorm(x) over the channels (x itself when ln_weight
@@ -332,5 +348,5 @@ __all__ = [
     "lib", "LIB_PATH", "Opts", "RwkvError", "header_functions", "status_string",
     "rwkv4_wkv_forward", "rwkv4_wkv_step", "rwkv4_timemix_fused", "rwkv_status_string",
     "rwkv_last_error", "rwkv4_workspace_bytes", "rwkv_abi_version", "rwkv4_shift_mix",
-    "rwkv4_channelmix_gate",
+    "rwkv4_channelmix_gate", "rwkv4_lookback_status",
 ]

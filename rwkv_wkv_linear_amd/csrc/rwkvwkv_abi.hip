@@ -35,33 +35,47 @@ rwkv_status hip_fail(hipError_t e, const char *where) {
     return fail(RWKV_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
-// Library-cached chunked-scan workspace, one per device, grown on demand.
-struct DeviceWorkspace {
-    void *ptr = nullptr;
-    size_t bytes = 0;
+// Library-cached chunked-scan workspace, one per (device, stream), grown on demand.  Calls on
+// one stream run in order, so they may share one; calls on different streams may run at once
+// and must not share the look-back words.
+struct CachedWorkspace {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
 };
 std::mutex g_ws_mu;
-std::vector<DeviceWorkspace> g_ws;
+std::vector<CachedWorkspace> g_ws;
 std::atomic<uint32_t> g_epoch{0};
 
 // Launch stamp in [1, 2^30 - 1]; a zero-filled workspace never matches it.
 uint32_t next_epoch() { return (g_epoch.fetch_add(1, std::memory_order_relaxed) % ((1u << 30) - 1u)) + 1u; }
+
+// The cached workspace of (current device, stream), or null if none was allocated yet.
+CachedWorkspace *find_cached(int dev, hipStream_t stream) {
+    for (CachedWorkspace &w : g_ws)
+        if (w.dev == dev && w.stream == stream) return &w;
+    return nullptr;
+}
 
 rwkv_status cached_workspace(size_t need, hipStream_t stream, void **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-    DeviceWorkspace &w = g_ws[dev];
-    if (w.bytes < need) {
-        if (w.ptr) {
-            // the old buffer may still be in use by enqueued work
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
+    CachedWorkspace *w = find_cached(dev, stream);
+    if (!w) {
+        g_ws.push_back(CachedWorkspace{dev, stream, nullptr, 0});
+        w = &g_ws.back();
+    }
+    if (w->bytes < need) {
+        if (w->ptr) {
+            // the old buffer may still be in use by work enqueued on the stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(w->ptr);
+            w->ptr = nullptr;
+            w->bytes = 0;
         }
         size_t nb = need < (1u << 20) ? (1u << 20) : need;
         void *p = nullptr;
@@ -72,10 +86,10 @@ rwkv_status cached_workspace(size_t need, hipStream_t stream, void **out) {
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync(workspace)");
         }
-        w.ptr = p;
-        w.bytes = nb;
+        w->ptr = p;
+        w->bytes = nb;
     }
-    *out = w.ptr;
+    *out = w->ptr;
     return RWKV_OK;
 }
 
@@ -207,16 +221,36 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         chunk = cmax;
     }
     const int64_t nTT = (T + chunk - 1) / chunk;
-    const bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
+    bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
+    if (T > chunk && o.workspace) {
+        const size_t need = chunk_workspace_bytes(B, T, C, chunk);
+        if (o.workspace_bytes < need)
+            return fail(RWKV_ERR_ARG, "workspace of %zu bytes is smaller than the %zu needed", o.workspace_bytes,
+                        need);
+    }
+    if (T > chunk) {
+        // A captured launch replays with the arguments of its capture.  The single pass stamps
+        // its look-back words with a per-launch epoch from the host, so a replay would accept
+        // the previous replay's words; under capture AUTO takes the two-pass scan instead, which
+        // needs no epoch, and the library-cached workspace (allocated on first use) is refused.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone) {
+            if (o.algo == RWKV_ALGO_CHUNKED)
+                return fail(RWKV_ERR_ARG, "RWKV_ALGO_CHUNKED cannot be captured into a graph (its look-back is "
+                                          "stamped per launch); use RWKV_ALGO_TWO_PASS or AUTO");
+            if (!o.workspace)
+                return fail(RWKV_ERR_ARG, "a chunked scan under stream capture needs opts->workspace "
+                                          "(the library-cached workspace is allocated on first use)");
+            two_pass = true;
+        }
+    }
     ChunkWorkspace ws{};
     if (T > chunk) {  // more than one tile per chain: the prefixes need scratch
         const size_t need = chunk_workspace_bytes(B, T, C, chunk);
-        void *base = o.workspace;
-        if (base) {
-            if (o.workspace_bytes < need)
-                return fail(RWKV_ERR_ARG, "workspace of %zu bytes is smaller than the %zu needed",
-                            o.workspace_bytes, need);
-        } else {
+        void *base = o.workspace;  // its size was checked above
+        if (!base) {
             rwkv_status s = cached_workspace(need, stream, &base);
             if (s != RWKV_OK) return s;
         }
@@ -444,6 +478,34 @@ size_t rwkv4_workspace_bytes(int64_t B, int64_t T, int64_t C, int32_t chunk_len)
     int chunk = chunk_len > 0 ? chunk_len : auto_chunk_len(B, T, C, 0);
     if (T <= chunk) return 0;
     return chunk_workspace_bytes(B, T, C, chunk);
+}
+
+rwkv_status rwkv4_lookback_status(void *workspace, hipStream_t stream, int32_t *gave_up) {
+    if (!gave_up) return fail(RWKV_ERR_ARG, "gave_up is required");
+    *gave_up = 0;
+    if (workspace && !aligned(workspace, 256)) return fail(RWKV_ERR_ALIGN, "workspace must be 256-byte aligned");
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    void *base = workspace;
+    if (!base) {
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        const CachedWorkspace *w = find_cached(dev, stream);
+        if (!w || !w->ptr) return ok();  // no chunked scan has run on this stream
+        base = w->ptr;
+    }
+    uint32_t word = 0;
+    e = hipMemcpy(&word, base, sizeof word, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+    if (word != 0) {
+        e = hipMemsetAsync(base, 0, sizeof word, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+        *gave_up = 1;
+    }
+    return ok();
 }
 
 int rwkv_abi_version(void) { return RWKV_ABI_VERSION; }

@@ -323,11 +323,14 @@ __device__ __forceinline__ void publish(const ChunkWorkspace &ws, int64_t tile, 
 
 // Fold of the published states of tiles [lo, hi) of a chain, left to right; tile lo is an
 // anchor (inclusive state) when lo_incl is set, every other tile an aggregate.  Every lane
-// loads its channel's fields of every tile and checks every tag.  While some are missing the
-// wave waits on one word per tile (lane m polls the last field of channel 0 of tile lo + m,
-// with a back-off) before reading everything again (a word written by the same store
-// instruction for another channel may become visible a little later than the polled one).
-// Returns NaNs if the wait gives up (then the failure shows in the outputs and ws.err is set).
+// loads its channel's fields of every tile and checks every tag; while some are missing the
+// wave reads all of them again, back to back (a state found in the same XCD's L2 costs one
+// short round trip, so a separate probe word followed by a second full read would only add one).
+// The workspace's error word is read with the first attempt and every 64th after it: once a
+// wait on the workspace has given up, every later wait gives up at once, in this launch and in
+// later ones, until the caller reads and clears the word (rwkv4_lookback_status).  A wait gives
+// up after kMaxSpins attempts too; it then stores the launch's epoch in the error word and
+// returns NaNs, so the failure shows in the outputs as well.
 template <int MAXT>
 __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo, int64_t hi, bool lo_incl,
                              float wc, float TW, int ch) {
@@ -335,9 +338,6 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
     const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
     uint64_t w[MAXT][4];
     const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
-    // Every attempt reads every word, back to back until all carry the expected tags: a state
-    // found in the same XCD's L2 costs one short round trip, so a separate probe followed by a
-    // second full read would only add one.
     auto read_all = [&]() -> bool {
         bool all = true;
 #pragma unroll
@@ -354,17 +354,21 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
         }
         return __all(all);
     };
+    auto error_set = [&]() -> bool {
+        const uint32_t e = __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_amdgcn_readfirstlane(e) != 0u;
+    };
+    bool failed = error_set();  // in flight together with the first attempt's loads
+    bool done = read_all();
     uint32_t spins = 0;
-    while (!read_all()) {
+    while (!done && !failed) {
         ++spins;
-        // give up after kMaxSpins, or at once when another wait of this launch has given up (the
-        // error word then holds the launch's epoch, so a failed launch leaves later launches on
-        // the same workspace unaffected)
-        if (spins > kMaxSpins ||
-            ((spins & 63u) == 0 && __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ws.epoch)) {
-            __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
-        }
+        failed = spins > kMaxSpins || ((spins & 63u) == 0 && error_set());
+        if (!failed) done = read_all();
+    }
+    if (failed) {
+        __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return St{__builtin_nanf(""), __builtin_nanf(""), 0.f, 0.f};
     }
     St acc = st_empty();
 #pragma unroll
@@ -384,6 +388,8 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 // (n <- e^w n + X v).  The guard keeps every surviving term a normal fp32 number:
 //   key spread kmax - kmin <= 40 nats and bonus u >= -20, so each current-token weight
 //   e^{u + k_t - kmax} >= e^{-60}, and anything flushed to zero is < 1e-12 of it;
+//   bonus u <= 30: the staged summary scales by the first group's largest key, so a weight may
+//   reach e^40, and e^u times it stays below e^70 (fp32 overflows past e^88);
 //   incoming state scale p - kmax <= 60, so it cannot overflow.
 // A lane outside the guard runs the exact per-token max-trick instead (same results within
 // rounding; the tests drive both paths).
@@ -413,6 +419,7 @@ constexpr int PREFIX_LOOKBACK = 0, PREFIX_AGGS = 1;
 
 constexpr float kGuardSpread = 40.f;
 constexpr float kGuardBonus = -20.f;
+constexpr float kGuardBonusMax = 30.f;
 constexpr float kGuardState = 60.f;
 
 // Phase A of a tile: wave wv stages its L rows (tokens t0 .. t0+L-1 of the tile) of each
@@ -493,7 +500,7 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
             kmin = fminf(kmin, i < nval ? xk[i] : INFINITY);
         }
     }
-    fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
+    fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus && uc <= kGuardBonusMax;
     if (fast) {
         float nn = 0.f, dd = 0.f;
         if (nval == L) {
@@ -577,7 +584,7 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
         }
     }
     static_assert(NG <= 4, "at most four groups per wave");
-    fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus;
+    fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus && uc <= kGuardBonusMax;
     mref = m;
     return St{nn, dd, m, 0.f};
 }

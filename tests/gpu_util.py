@@ -18,10 +18,11 @@ OUT_TOL = {"f32": 0.0, "f16": 0.0, "bf16": 8e-3}
 
 def tol_for(in_dtype: str, out_dtype: str) -> float:
     return max(TOL[in_dtype], OUT_TOL[out_dtype])
-# The fp32 state has no numerator/denominator cancellation: rounding accumulates over the
-# decay window, 1 / (1 - e^w) ~ 149 tokens for the slowest channel (w = -e^-5), at about
-# 4 roundings of 2^-24 per token -> 3.6e-5.  The state bar is this bound, rounded up.
-STATE_TOL_FLOOR = 5e-5
+# The state is fp32 arithmetic on inputs that the oracle reads exactly (the same rounded
+# values), and it is never rounded to the I/O dtype, so the input dtype does not enter its error:
+# one bar for every input dtype, the fp32 bar.  aa is measured against the oracle's |aa|
+# accumulator and bb (a sum of positive weights, no cancellation) against itself.
+STATE_TOL = 1e-5
 CANARY = 4096                       # elements after each output that must stay untouched
 CANARY_VALUE = 1232.0               # exact in fp32, fp16 and bfloat16 (7 significant bits)
 
@@ -91,8 +92,9 @@ def check_output(y, ref, tol, what, argmax=True, out_dtype="f32"):
     return rep
 
 
-def check_state(state, ref, tol, what):
-    tol = max(tol, STATE_TOL_FLOOR)
+def check_state(state, ref, what):
+    """Gate of a final state (compared canonically, see oracle.compare.state_error)."""
     ea, eb = cmp.state_error(state, ref["state"], ref["state_abs"])
     note(f"{what}: state err aa {ea:.3e} bb {eb:.3e}")
-    assert ea <= tol and eb <= tol, f"{what}: state error aa {ea:.3e} bb {eb:.3e} > {tol:.1e}"
+    assert ea <= STATE_TOL and eb <= STATE_TOL, \
+        f"{what}: state error aa {ea:.3e} bb {eb:.3e} > {STATE_TOL:.1e}"

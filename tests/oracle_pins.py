@@ -37,13 +37,17 @@ def _rng(seed):
 
 
 def _parse(expr):
-    """Evaluate the golden file's tiny expression language: numbers, ln(a), ln(a/b), -ln(a)."""
+    """Evaluate the golden files' tiny expression language: numbers, a/b, ln(a), ln(a/b), -ln(a)
+    and c*ln(a) (c a number)."""
     if isinstance(expr, (int, float)):
         return float(expr)
     e = expr.strip()
     sign = 1.0
     if e.startswith("-"):
         sign, e = -1.0, e[1:]
+    if "*" in e:
+        c, rest = e.split("*", 1)
+        return sign * float(c) * _parse(rest)
     if e.startswith("ln(") and e.endswith(")"):
         inner = e[3:-1]
         if "/" in inner:
@@ -100,11 +104,65 @@ def pin_hand_worked():
         exp_state = case["state_out"]
         _close(so.ravel(), [exp_state["aa"], exp_state["bb"], exp_state["pp"]], 1e-14,
                f"hand-worked state '{case['name']}'")
+        # the forward's composition (gated WKV and the state after the tokens) on the same case
+        out = oracle.forward(dict(k=k, v=v, w=w, u=u, r=r, state_in=st))
+        _close(out["y"].ravel(), want, 1e-14, f"hand-worked forward '{case['name']}'")
+        _close(out["state"].ravel(), [exp_state["aa"], exp_state["bb"], exp_state["pp"]], 1e-14,
+               f"hand-worked forward state '{case['name']}'")
     ts = g["token_shift"]
     x = np.array(ts["x"], dtype=np.float64).reshape(1, 3, 1)
     out = oracle.token_shift(x, np.array([[ts["x_prev"]]], dtype=np.float64),
                              np.array([ts["mix"]]))
     _close(out.ravel(), ts["out"], 1e-15, "hand-worked token shift")
+
+
+def _golden_timemix():
+    with open(os.path.join(GOLDEN, "timemix_hand_worked.json")) as f:
+        return json.load(f)
+
+
+def _grid(rows):
+    return np.array([[_parse(e) for e in row] for row in rows], dtype=np.float64)
+
+
+def pin_timemix_hand_worked():
+    """The composition token shift -> r := xr -> gated WKV over the given k, v -> x_last, against
+    a case worked by hand (tests/golden/timemix_hand_worked.json), with distinct mix_r, mix_k and
+    mix_v so that a mix or a shifted stream taken in the wrong place changes the result."""
+    g = _golden_timemix()["timemix"]
+    T, C = g["T"], g["C"]
+    case = dict(x=_grid(g["x"]).reshape(1, T, C), x_prev=np.array([[_parse(e) for e in g["x_prev"]]]),
+                mix_k=np.array(g["mix_k"], float), mix_v=np.array(g["mix_v"], float),
+                mix_r=np.array(g["mix_r"], float), k=_grid(g["k"]).reshape(1, T, C),
+                v=np.array(g["v"], float).reshape(1, T, C), w=np.array([_parse(e) for e in g["w"]]),
+                u=np.array([_parse(e) for e in g["u"]]), state_in=None)
+    so = g["state_out"]
+    want_state = np.array([[_parse(e) for e in so[f]] for f in ("aa", "bb", "pp")]).reshape(3, 1, C)
+    for method in ("recurrence", "direct"):
+        out = oracle.timemix(case, method=method)
+        _close(out["y"][0], _grid(g["y"]), 1e-14, f"time-mix hand-worked y ({method})")
+        for name in ("xr", "xk", "xv"):
+            _close(out[name][0], _grid(g[name]), 1e-14, f"time-mix hand-worked {name}")
+        _close(out["x_last"][0], [_parse(e) for e in g["x_last"]], 0, "time-mix hand-worked x_last")
+        _close(out["state"], want_state, 1e-14, "time-mix hand-worked state")
+    # the receptance is the shifted mix itself: ungated WKV times the logistic of xr
+    y0, _ = oracle.wkv_direct(case["k"], case["v"], case["w"], case["u"])
+    _close(y0[0], _grid(g["wkv"]), 1e-14, "time-mix hand-worked ungated WKV")
+
+
+def pin_step_hand_worked():
+    """One decode token from a prior state (the T = 1 case of the forward), worked by hand."""
+    g = _golden_timemix()["step"]
+    st = g["state"]
+    layer = dict(w=np.array([_parse(g["w"])]), u=np.array([_parse(g["u"])]),
+                 k=np.array([[_parse(g["k"])]]), v=np.array([[float(g["v"])]]),
+                 r=np.array([[_parse(g["r"])]]),
+                 state=np.array([_parse(st["aa"]), _parse(st["bb"]), _parse(st["pp"])]).reshape(3, 1, 1))
+    out = oracle.step(layer)
+    _close(out["y"].ravel(), [_parse(g["y"])], 1e-15, "step hand-worked y")
+    so = g["state_out"]
+    _close(out["state"].ravel(), [_parse(so["aa"]), _parse(so["bb"]), _parse(so["pp"])], 1e-15,
+           "step hand-worked state")
 
 
 # ----------------------------------------------------------------------------- closed forms
@@ -424,5 +482,5 @@ ALL_PINS = [
     pin_state_split_carry, pin_state_canonical, pin_direct_vs_recurrence,
     pin_points_match_direct, pin_mpmath_precision, pin_layer_norm_hand_worked,
     pin_layer_norm_moments, pin_layer_norm_library, pin_layer_norm_invariance,
-    pin_shift_mix_hand_worked, pin_receptance_gate,
+    pin_shift_mix_hand_worked, pin_receptance_gate, pin_timemix_hand_worked, pin_step_hand_worked,
 ]

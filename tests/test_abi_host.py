@@ -218,3 +218,18 @@ def test_channelmix_gate_validation():
     assert gate(y=p(0x200010)) == rw.RWKV_ERR_ARG                    # y inside kv
     assert gate(y=p(0x300010)) == rw.RWKV_ERR_ARG                    # y partly over the residual
     assert gate(i=1, o=0, y=p(0x300000)) == rw.RWKV_ERR_ARG          # in place needs equal dtypes
+
+
+def test_lookback_status_validation():
+    flag = ctypes.c_int32(7)
+    assert L.rwkv4_lookback_status(p(0), None, None) == rw.RWKV_ERR_ARG
+    assert "gave_up" in rw.rwkv_last_error()
+    assert L.rwkv4_lookback_status(p(4), None, ctypes.byref(flag)) == rw.RWKV_ERR_ALIGN
+    assert flag.value == 0  # cleared before any check that fails
+
+
+def test_chunked_workspace_size_checked_before_any_hip_call():
+    # the capture query and the cached workspace come after every host-side check
+    o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, algo=rw.RWKV_ALGO_TWO_PASS,
+             workspace=P + 0x800000, workspace_bytes=255)
+    assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "workspace" in rw.rwkv_last_error()

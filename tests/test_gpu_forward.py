@@ -61,7 +61,7 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     y, st = run(case, algo, chunk, label="ragged")
     tol = TOL[in_dt] if out_dt == "f32" or in_dt == "f16" else TOL["f16"]
     check_output(y, ref, tol, f"ragged {in_dt}->{out_dt} {algo}/{chunk}", out_dtype=out_dt)
-    check_state(st, ref, TOL[in_dt], f"ragged {in_dt} {algo}/{chunk}")
+    check_state(st, ref, f"ragged {in_dt} {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
@@ -72,7 +72,7 @@ def test_odd_channels(C, algo, chunk):
     ref = oracle_forward(("odd", C), case)
     y, st = run(case, algo, chunk, label=f"odd C={C}")
     check_output(y, ref, TOL["f16"], f"C={C} {algo}/{chunk}", argmax=C > 1, out_dtype="f16")
-    check_state(st, ref, TOL["f16"], f"C={C} {algo}/{chunk}")
+    check_state(st, ref, f"C={C} {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("two_pass", 64)])
@@ -99,7 +99,7 @@ def test_misaligned_pointers(algo, chunk):
                          state_out=so, r=r, algo=algo, chunk_len=chunk)
     t.cuda.synchronize()
     check_output(host(y), ref, TOL["f16"], f"misaligned {algo}", out_dtype="f16")
-    check_state(host(so), ref, TOL["f16"], f"misaligned {algo}")
+    check_state(host(so), ref, f"misaligned {algo}")
 
 
 @pytest.mark.parametrize("algo", ["sequential", "chunked", "two_pass"])
@@ -108,7 +108,7 @@ def test_single_token(algo):
     ref = oracle.forward(case, method="direct")
     y, st = run(case, algo, 0 if algo == "sequential" else 64, label="T=1")
     check_output(y, ref, TOL["f32"], f"T=1 {algo}")
-    check_state(st, ref, TOL["f32"], f"T=1 {algo}")
+    check_state(st, ref, f"T=1 {algo}")
 
 
 def test_zero_tokens_copies_state():
@@ -142,7 +142,7 @@ def test_state_in_place_and_null_state():
                              y=y, state_in=st, state_out=st, r=to_dev(case["r"]), algo=algo, chunk_len=chunk)
         t.cuda.synchronize()
         check_output(host(y), ref, TOL["f16"], f"in-place {algo}/{chunk}", out_dtype="f16")
-        check_state(host(st), ref, TOL["f16"], f"in-place {algo}/{chunk}")
+        check_state(host(st), ref, f"in-place {algo}/{chunk}")
         y2 = t.empty_like(y)
         rw.rwkv4_wkv_forward(to_dev(case["k"]), to_dev(case["v"]), to_dev(case["w"]), to_dev(case["u"]),
                              y=y2, state_in=to_dev(case["state_in"]), state_out=None,
@@ -159,7 +159,7 @@ def test_full_forgetting_channels():
     for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, st = run(case, algo, chunk, label="w=-inf")
         check_output(y, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
-        check_state(st, ref, TOL["f32"], f"w=-inf {algo}/{chunk}")
+        check_state(st, ref, f"w=-inf {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("shift", [100.0, -100.0])
@@ -175,7 +175,7 @@ def test_shift_invariance_needs_max_trick(shift):
     for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, s = run(case, algo, chunk, label=f"shift {shift}")
         check_output(y, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
-        check_state(s, ref, TOL["f32"], f"shift {shift} {algo}/{chunk}")
+        check_state(s, ref, f"shift {shift} {algo}/{chunk}")
 
 
 def test_wide_key_spread():
@@ -187,7 +187,7 @@ def test_wide_key_spread():
     for algo, chunk in (("sequential", 0), ("chunked", 64), ("two_pass", 64)):
         y, s = run(case, algo, chunk, label="wide spread")
         check_output(y, ref, TOL["f32"], f"spread {algo}/{chunk}")
-        check_state(s, ref, TOL["f32"], f"spread {algo}/{chunk}")
+        check_state(s, ref, f"spread {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("in_dt", ["f16", "bf16"])
@@ -206,7 +206,49 @@ def test_wide_key_spread_2byte_staged(in_dt):
     for algo, chunk in (("chunked", 128), ("two_pass", 128)):
         y, s = run(case, algo, chunk, label=f"wide spread {in_dt}")
         check_output(y, ref, TOL[in_dt], f"spread {in_dt} {algo}/{chunk}")
-        check_state(s, ref, TOL[in_dt], f"spread {in_dt} {algo}/{chunk}")
+        check_state(s, ref, f"spread {in_dt} {algo}/{chunk}")
+
+
+GUARD_ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)]
+
+
+@pytest.mark.parametrize("in_dt", ["f32", "f16"])
+@pytest.mark.parametrize("algo,chunk", GUARD_ALGOS)
+def test_bonus_outside_the_linear_space_guard(in_dt, algo, chunk):
+    """Channels with u = -25 (below the fast path's bonus guard: the current token's weight would
+    underflow against the others) and u = +40 (above it: e^u times a weight of up to e^40
+    overflows fp32) take the exact per-token recurrence; their neighbours stay on the fast path."""
+    if in_dt == "f32" and chunk > 64:
+        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
+    case = wi.forward_case(2, 1000, 192, seed=54, in_dtype=in_dt, out_dtype="f32", gated=True, prior=True)
+    u = case["u"].copy()
+    u[0::5] = -25.0
+    u[2::5] = 40.0
+    case["u"] = u
+    ref = oracle_forward(("bonus guard", in_dt), case)
+    y, st = run(case, algo, chunk, label=f"bonus guard {in_dt}")
+    check_output(y, ref, TOL[in_dt], f"bonus guard {in_dt} {algo}/{chunk}")
+    check_state(st, ref, f"bonus guard {in_dt} {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("in_dt", ["f32", "f16"])
+@pytest.mark.parametrize("algo,chunk", GUARD_ALGOS)
+def test_incoming_state_outside_the_linear_space_guard(in_dt, algo, chunk):
+    """One key of +70 early in the slowest-decaying channels, then N(0,1) keys: the chain's state
+    keeps a log-scale near 70 - 0.0067 n for thousands of tokens, so the waves of later tiles
+    start more than 60 nats above their own largest key (the incoming-state guard) and take the
+    exact recurrence, until the scale has decayed back inside the guard (after ~1000 tokens)."""
+    if in_dt == "f32" and chunk > 64:
+        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
+    case = wi.forward_case(1, 2048, 128, seed=55, in_dtype=in_dt, out_dtype="f32", prior=False)
+    k = case["k"].astype(np.float64)
+    k[0, 5, 0:8] = 70.0
+    k[0, 700, 64:66] = 66.0   # a second tile's worth of large states in another channel tile
+    case["k"] = wi._as(k, in_dt)
+    ref = oracle_forward(("state guard", in_dt), case)
+    y, st = run(case, algo, chunk, label=f"state guard {in_dt}")
+    check_output(y, ref, TOL[in_dt], f"state guard {in_dt} {algo}/{chunk}")
+    check_state(st, ref, f"state guard {in_dt} {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("algo", ["chunked", "two_pass"])
@@ -227,7 +269,7 @@ def test_split_sequence_carry(algo):
     t.cuda.synchronize()
     y = np.concatenate([host(y1), host(y2)], axis=1)
     check_output(y, ref, TOL["f32"], f"split carry {algo}")
-    check_state(host(st), ref, TOL["f32"], f"split carry {algo}")
+    check_state(host(st), ref, f"split carry {algo}")
 
 
 @pytest.mark.parametrize("B,T,C", [(3, 700, 512), (1, 900, 1024)])
@@ -239,21 +281,25 @@ def test_chain_order_across_xcds(B, T, C, algo, chunk):
     ref = oracle_forward(("xcd order", B, T, C), case)
     y, st = run(case, algo, chunk, label="xcd order")
     check_output(y, ref, TOL["f16"], f"xcd order B{B} T{T} C{C} {algo}/{chunk}", out_dtype="f16")
-    check_state(st, ref, TOL["f16"], f"xcd order B{B} T{T} C{C} {algo}/{chunk}")
+    check_state(st, ref, f"xcd order B{B} T{T} C{C} {algo}/{chunk}")
 
 
-@pytest.mark.parametrize("algo", ["chunked", "two_pass"])
-def test_deterministic(algo):
+@pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("two_pass", 64), ("chunked", 128), ("two_pass", 128),
+                                        ("auto", 0)])
+def test_deterministic(algo, chunk):
+    """Two runs give bitwise equal outputs and states (the look-back folds its predecessors in a
+    fixed order whatever the timing); auto takes the 128-token single pass that the fp16
+    workloads run."""
     import rwkv_wkv_linear_amd as rw
     t = torch()
     case = wi.forward_case(2, 2048, 256, seed=51, in_dtype="f16", gated=True, prior=True)
     args = [to_dev(case[n]) for n in ("k", "v", "w", "u")]
     outs = []
     for _ in range(2):
-        note(f"forward determinism {algo}")
+        note(f"forward determinism {algo}/{chunk}")
         so = t.empty((3, 2, 256), device="cuda:0")
         y = rw.rwkv4_wkv_forward(*args, state_in=to_dev(case["state_in"]), state_out=so,
-                                 r=to_dev(case["r"]), algo=algo, chunk_len=64)
+                                 r=to_dev(case["r"]), algo=algo, chunk_len=chunk)
         t.cuda.synchronize()
         outs.append((y.clone(), so.clone()))
     assert t.equal(outs[0][0], outs[1][0]) and t.equal(outs[0][1], outs[1][1])
@@ -291,7 +337,7 @@ def test_workload_169m_fp32(algo, chunk):
     ref = oracle_forward("w0", case, method="direct")
     y, st = run(case, algo, chunk, label="rwkv4-169m fp32")
     check_output(y, ref, TOL["f32"], f"169m fp32 {algo}/{chunk}")
-    check_state(st, ref, TOL["f32"], f"169m fp32 {algo}/{chunk}")
+    check_state(st, ref, f"169m fp32 {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("algo,chunk", ALGOS)
@@ -309,4 +355,4 @@ def test_workload_169m_batch_f16(algo, chunk):
         _cache["w1pts"] = True
     y, st = run(case, algo, chunk, label="rwkv4-169m batch f16")
     check_output(y, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}", out_dtype="f16")
-    check_state(st, ref, TOL["f16"], f"169m batch f16 {algo}/{chunk}")
+    check_state(st, ref, f"169m batch f16 {algo}/{chunk}")

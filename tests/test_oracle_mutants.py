@@ -84,3 +84,50 @@ def test_mutant_is_caught(workdir, name, old, new, every):
     finally:
         oracle._restore_library(prev)
     assert failed, f"mutant '{name}' passed every pin"
+
+
+# Planted mistakes in the oracle's Python composition (oracle/__init__.py): each is one edit of a
+# function's source, compiled in the module's namespace and swapped in for the original while
+# the pins run.  (function, name, text in the function, replacement)
+PY_MUTANTS = [
+    ("timemix", "receptance taken from xk", "r=xr,", "r=xk,"),
+    ("timemix", "xr mixed with mix_k", 'xr = token_shift(x, xp, case["mix_r"])',
+     'xr = token_shift(x, xp, case["mix_k"])'),
+    ("timemix", "x_prev dropped from the receptance shift", 'xr = token_shift(x, xp,', 'xr = token_shift(x, None,'),
+    ("timemix", "x_last from the first row", "_f64(x)[:, -1, :]", "_f64(x)[:, 0, :]"),
+    ("timemix", "k and v swapped in the WKV", 'fn(case["k"], case["v"], case["w"], case["u"], r=xr',
+     'fn(case["v"], case["k"], case["w"], case["u"], r=xr'),
+    ("timemix", "xk output mixed with mix_v", 'xk = token_shift(x, xp, case["mix_k"])',
+     'xk = token_shift(x, xp, case["mix_v"])'),
+    ("timemix", "xv output unshifted", 'xv = token_shift(x, xp, case["mix_v"])', 'xv = _f64(x)'),
+    ("timemix", "state of the gate stream", 'st, ab = wkv_state(case["k"], case["v"]', 'st, ab = wkv_state(case["k"], xr'),
+    ("forward", "gate dropped", 'r=case.get("r"),', "r=None,"),
+    ("forward", "prior state left out of the state", 'st, ab = wkv_state(case["k"], case["v"], case["w"], state_in=case.get("state_in")',
+     'st, ab = wkv_state(case["k"], case["v"], case["w"], state_in=None'),
+    ("step", "gate dropped", 'r=r, state_in=layer["state"]', 'r=None, state_in=layer["state"]'),
+    ("step", "prior state ignored by the output", 'r=r, state_in=layer["state"]', 'r=r, state_in=None'),
+    ("shift_mix", "shift of the raw rows", "token_shift(ln, xp, case[mix])", "token_shift(x, xp, case[mix])"),
+    ("shift_mix", "x_last from the raw row", 'out["x_last"] = ln[:, -1, :].copy()', 'out["x_last"] = x[:, -1, :].copy()'),
+]
+
+
+@pytest.mark.parametrize("func,name,old,new", PY_MUTANTS, ids=[f"{m[0]}: {m[1]}" for m in PY_MUTANTS])
+def test_composition_mutant_is_caught(func, name, old, new):
+    import inspect
+    import textwrap
+    orig = getattr(oracle, func)
+    src = textwrap.dedent(inspect.getsource(orig))
+    assert old in src, f"mutation site for '{name}' not found in oracle.{func}"
+    ns = {}
+    exec(compile(src.replace(old, new, 1), f"<mutant of oracle.{func}>", "exec"), vars(oracle), ns)
+    setattr(oracle, func, ns[func])
+    failed = []
+    try:
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin()
+            except Exception:
+                failed.append(pin.__name__)
+    finally:
+        setattr(oracle, func, orig)
+    assert failed, f"mutant '{func}: {name}' passed every pin"
