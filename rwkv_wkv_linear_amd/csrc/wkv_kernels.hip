@@ -354,17 +354,18 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
         }
         return __all(all);
     };
-    auto error_set = [&]() -> bool {
-        const uint32_t e = __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return __builtin_amdgcn_readfirstlane(e) != 0u;
-    };
-    bool failed = error_set();  // in flight together with the first attempt's loads
-    bool done = read_all();
-    uint32_t spins = 0;
-    while (!done && !failed) {
-        ++spins;
-        failed = spins > kMaxSpins || ((spins & 63u) == 0 && error_set());
-        if (!failed) done = read_all();
+    // one read site (a second inlined copy of read_all would hold a second set of words)
+    bool failed = false;
+    for (uint32_t spins = 0;; ++spins) {
+        const bool check = (spins & 63u) == 0u;
+        uint32_t e = 0;
+        if (check) e = __hip_atomic_load(ws.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // with the reads
+        const bool done = read_all();
+        if ((check && __builtin_amdgcn_readfirstlane(e) != 0u) || (!done && spins >= kMaxSpins)) {
+            failed = true;
+            break;
+        }
+        if (done) break;
     }
     if (failed) {
         __hip_atomic_store(ws.err, ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -386,13 +387,15 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
 // weight by e^{-kmax}, kmax the largest key of its tokens; the weights e^{k_i - kmax} are then
 // at most 1, computed once, and the numerator/denominator run as plain fp32 recurrences
 // (n <- e^w n + X v).  The guard keeps every surviving term a normal fp32 number:
-//   key spread kmax - kmin <= 40 nats and bonus u >= -20, so each current-token weight
-//   e^{u + k_t - kmax} >= e^{-60}, and anything flushed to zero is < 1e-12 of it;
-//   bonus u <= 30: the staged summary scales by the first group's largest key, so a weight may
-//   reach e^40, and e^u times it stays below e^70 (fp32 overflows past e^88);
-//   incoming state scale p - kmax <= 60, so it cannot overflow.
+//   key spread kmax - kmin <= 40 nats (the summary and the emit): every weight lies in
+//   [e^-40, 1], or in [e^-40, e^40] when the staged summary scales by its first group's
+//   largest key;
+//   bonus -20 <= u <= 30 (the emit): each current-token weight e^{u + k_t - kmax} is at least
+//   e^{-60}, so anything flushed to zero is < 1e-12 of it, and at most e^70 (fp32 overflows
+//   past e^88);
+//   incoming state scale p - kmax <= 60 (the emit), so it cannot overflow.
 // A lane outside the guard runs the exact per-token max-trick instead (same results within
-// rounding; the tests drive both paths).
+// rounding; the tests drive both paths, and waves whose lanes take different paths).
 // Workgroups are handed to the eight XCDs round-robin by index, so blockIdx % 8 picks a
 // workgroup's XCD.  When nCT is a multiple of 8, the plain order (r = b * nCT + ct) gives each
 // XCD every eighth chain, all in the same 128-byte column of every 1 KB of each row, and the
@@ -473,7 +476,7 @@ __device__ __forceinline__ void stage_rows(const TIn *const *src, TIn *rows, int
 // Phase B of a tile: the summary of one wave's nval tokens from the empty state (kr, vr point
 // at the lane's first staged key and value).  Padded tokens (i >= nval) get weight X = 0 and
 // decay 1, so they leave every recurrence unchanged.  Sets kmax (the largest key) and fast
-// (whether the linear-space guard holds; else the exact per-token max-trick ran).
+// (whether the key-spread part of the linear-space guard holds; else the exact per-token max-trick ran).
 template <typename TIn, int L>
 __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nval, float wc, float uc, float ew,
                                            float &kmax, bool &fast, float (&Xs)[L]) {
@@ -500,7 +503,7 @@ __device__ __forceinline__ St wave_summary(const TIn *kr, const TIn *vr, int nva
             kmin = fminf(kmin, i < nval ? xk[i] : INFINITY);
         }
     }
-    fast = nval > 0 && (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus && uc <= kGuardBonusMax;
+    fast = nval > 0 && (kmax - kmin) <= kGuardSpread;
     if (fast) {
         float nn = 0.f, dd = 0.f;
         if (nval == L) {
@@ -584,7 +587,7 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
         }
     }
     static_assert(NG <= 4, "at most four groups per wave");
-    fast = (kmax - kmin) <= kGuardSpread && uc >= kGuardBonus && uc <= kGuardBonusMax;
+    fast = (kmax - kmin) <= kGuardSpread;
     mref = m;
     return St{nn, dd, m, 0.f};
 }
@@ -910,17 +913,21 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
     }
     const float pst = st_logmax(st, wc);
+    // the lane's tokens take the linear-space path; a wave whose lanes all do may stage y
+    const bool lane_fast = fast && pst - kmax <= kGuardState && uc >= kGuardBonus && uc <= kGuardBonusMax;
+    const bool wave_fast = __all(lane_fast);  // voted before the lanes diverge
     St fin;
-    if (fast && pst - kmax <= kGuardState) {
+    if (lane_fast) {
         const float s0 = ex(pst - kmax);
         float nn = st.a * s0, dd = st.b * s0;
         // rows as wave-uniform pointers plus a 32-bit lane offset
         const int64_t row0 = (b * a.T + t0) * C + ct * CW;
         const unsigned Cu = (unsigned)C;
-        // a full wave (all L tokens, all 64 channels in range) stages y in its own v rows,
-        // dead once v is in registers, and writes 16 bytes per lane
+        // a full wave (all L tokens, all 64 channels in range, every lane on this path) stages y
+        // in its own v rows, dead once v is in registers, and writes 16 bytes per lane: each
+        // lane's store carries other lanes' channels, so no lane may be on the exact path
         constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
-        const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16;
+        const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16 && wave_fast;
         TOut *ystage = reinterpret_cast<TOut *>(rows + ((size_t)1 * TW + wv * L) * CW);
         if (nval == L) {
             const bool mix = (MODE == MODE_TIMEMIX) && (XKO || XVO);

@@ -43,7 +43,7 @@ def test_forced_give_up_is_reported_and_cleared(chunk):
     t.cuda.synchronize()
     yh = host(y)
     assert np.all(np.isnan(yh[:, chunk:])), "a tile that waited produced numbers"
-    assert np.all(np.isnan(host(so))), "the final state came from a tile that waited"
+    assert np.all(np.isnan(host(so)[:2])), "the final state came from a tile that waited"
     first = dict(ref, y=ref["y"][:, :chunk], scale=ref["scale"][:, :chunk])
     check_output(yh[:, :chunk], first, TOL["f16"], f"first time tile under a forced give-up chunk={chunk}",
                  out_dtype="f16")
