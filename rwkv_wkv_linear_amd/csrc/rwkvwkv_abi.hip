@@ -212,16 +212,13 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         if (e != hipSuccess) return hip_fail(e, "launch (sequential)");
         return ok();
     }
-    int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, ei == 2);
-    const int cmax = chunk_max_len(ei == 2, a.mode);
-    if (chunk > cmax) {
-        if (o.chunk_len)
-            return fail(RWKV_ERR_ARG, "chunk_len %d exceeds %d, the largest tile this dtype/mode supports",
-                        chunk, cmax);
-        chunk = cmax;
-    }
+    const int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, ei == 2);
+    const int tmax = tile_max_len(ei == 2);
     const int64_t nTT = (T + chunk - 1) / chunk;
     bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
+    if (two_pass && chunk > tmax)
+        return fail(RWKV_ERR_ARG, "the two-pass scan takes chunk_len up to %d for this input dtype (got %d); longer "
+                                  "chunks run in the single-launch scan", tmax, chunk);
     if (T > chunk && o.workspace) {
         const size_t need = chunk_workspace_bytes(B, T, C, chunk);
         if (o.workspace_bytes < need)
@@ -237,9 +234,10 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         e = hipStreamIsCapturing(stream, &cap);
         if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
         if (cap != hipStreamCaptureStatusNone) {
-            if (o.algo == RWKV_ALGO_CHUNKED)
-                return fail(RWKV_ERR_ARG, "RWKV_ALGO_CHUNKED cannot be captured into a graph (its look-back is "
-                                          "stamped per launch); use RWKV_ALGO_TWO_PASS or AUTO");
+            if (o.algo == RWKV_ALGO_CHUNKED || chunk > tmax)
+                return fail(RWKV_ERR_ARG, "the single-launch chunked scan (RWKV_ALGO_CHUNKED, or a chunk_len above "
+                                          "%d) cannot be captured into a graph: its look-back is stamped per "
+                                          "launch", tmax);
             if (!o.workspace)
                 return fail(RWKV_ERR_ARG, "a chunked scan under stream capture needs opts->workspace "
                                           "(the library-cached workspace is allocated on first use)");

@@ -54,15 +54,18 @@ struct ForwardArgs {
 struct ChunkWorkspace {
     uint64_t *words;  // single pass: [tiles][4][64] tagged words
     float *aggs;      // two passes: [tiles][64][4] tile aggregates
-    uint32_t *err;    // one word: the epoch of a launch in which a look-back wait gave up
+    uint32_t *err;    // one word, nonzero once a look-back wait gave up (that launch's epoch),
+                      // until rwkv4_lookback_status clears it
     uint32_t epoch;   // per-launch stamp; words of other launches never match
 };
 
 constexpr int kTileChannels = 64;  // channels per workgroup tile
 constexpr int kMinChunk = 64, kMaxChunk = 1024;
 
-// Largest chunk length the chunked kernel supports for a dtype/mode (its register budget).
-int chunk_max_len(int in_2byte, int mode);
+// Longest tile whose rows are staged in LDS at once: 128 tokens for 2-byte inputs, 64 for fp32.
+// The two-pass scan takes chunk lengths up to it; the single-launch scan runs longer chunks (up
+// to kMaxChunk) as long tiles of such sub-tiles.
+int tile_max_len(int in_2byte);
 // Chunk length (tokens per workgroup tile) the auto policy picks for a shape.
 int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_2byte);
 // True when the auto policy picks the sequential kernel.

@@ -669,6 +669,143 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
     if constexpr (MODE == MODE_TIMEMIX && !MIX) xs = (float)gr[(L - 1) * CW];
 }
 
+// Phase B of a tile: the summary of the wave's tokens from the empty state, with only this
+// wave's k and v rows in flight.  A full wave whose rows come by 16-byte DMA takes them group by
+// group as they land (wave-uniform choice); lanes past C then drop their summary (their rows
+// are a copy of channel 0), and lanes outside the key-spread guard redo it exactly.  Otherwise
+// the wave waits for its rows and runs wave_summary.
+template <typename TIn, int L>
+__device__ __forceinline__ St summarize_wave(const TIn *kr, const TIn *vr, int wlen, int nval, bool cok, bool vec16,
+                                             float wc, float uc, float ew, float &kmax, bool &fast, float (&Xs)[L]) {
+    constexpr int CW = kTileChannels;
+    St sum;
+    if (vec16 && wlen == L) {
+        sum = wave_summary_staged<TIn, L>(kr, vr, ew, uc, kmax, fast, Xs);
+        if (!cok) {
+            sum = st_empty();
+            fast = false;
+        } else if (!fast) {
+            // outside the linear-space guard: the exact per-token recurrence (all rows landed)
+            sum = st_empty();
+#pragma unroll 1
+            for (int i = 0; i < L; ++i) absorb(sum, wc, (float)kr[i * CW], (float)vr[i * CW]);
+        }
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+        __builtin_amdgcn_wave_barrier();
+        sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
+    }
+    return sum;
+}
+
+// Phase E of a tile: emit y (and the time mix's xk, xv) for the wave's tokens starting from the
+// state st, and return the state after them.  kr, vr, gr point at the lane's first staged key,
+// value and gate row, vrow0 at the wave's first v row (y is staged there); Xs holds the weights
+// of the linear-space summary (fast), kmax their reference key; xs is the time mix's previous
+// token, updated to the wave's last.  base is the element offset of the lane's first token.
+template <typename TIn, typename TOut, int MODE, int L>
+__device__ __forceinline__ St emit_wave(const ForwardArgs &a, const St &st, const float (&Xs)[L], bool fast,
+                                        float kmax, const TIn *kr, const TIn *vr, const TIn *gr, TIn *vrow0,
+                                        float wc, float uc, float ew, float eu, float ga, float gb, float mk,
+                                        float mv, float &xs, int64_t b, int64_t ct, int64_t t0, int wlen, int nval,
+                                        int64_t base, int lane) {
+    constexpr int CW = kTileChannels;
+    const int64_t C = a.C;
+    TOut *Y = static_cast<TOut *>(a.y);
+    TIn *XKO = static_cast<TIn *>(a.xk_out);
+    TIn *XVO = static_cast<TIn *>(a.xv_out);
+    const float pst = st_logmax(st, wc);
+    // the lane's tokens take the linear-space path; a wave whose lanes all do may stage y
+    const bool lane_fast = fast && pst - kmax <= kGuardState && uc >= kGuardBonus && uc <= kGuardBonusMax;
+    const bool wave_fast = __all(lane_fast);  // voted before the lanes diverge
+    St fin;
+    if (lane_fast) {
+        const float s0 = ex(pst - kmax);
+        float nn = st.a * s0, dd = st.b * s0;
+        // rows as wave-uniform pointers plus a 32-bit lane offset
+        const int64_t row0 = (b * a.T + t0) * C + ct * CW;
+        const unsigned Cu = (unsigned)C;
+        // a full wave (all L tokens, all 64 channels in range, every lane on this path) stages y
+        // in its own v rows, dead once v is in registers, and writes 16 bytes per lane: each
+        // lane's store carries other lanes' channels, so no lane may be on the exact path
+        constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
+        const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16 && wave_fast;
+        TOut *ystage = reinterpret_cast<TOut *>(vrow0);
+        if (nval == L) {
+            const bool mix = (MODE == MODE_TIMEMIX) && (XKO || XVO);
+            TOut *yrow = Y + row0;
+            TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
+#define RWKV_EMIT(STAGE, MIX)                                                                          \
+    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
+                                                   xkrow, xvrow, ystage, Cu, lane)
+            if constexpr (MODE == MODE_TIMEMIX) {
+                if (stage_y) {
+                    if (mix) RWKV_EMIT(true, true); else RWKV_EMIT(true, false);
+                } else {
+                    if (mix) RWKV_EMIT(false, true); else RWKV_EMIT(false, false);
+                }
+            } else {
+                if (stage_y) RWKV_EMIT(true, false); else RWKV_EMIT(false, false);
+            }
+#undef RWKV_EMIT
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const float kk = (float)kr[i * CW], vv = (float)vr[i * CW];
+                const float X = (i < nval) ? ex(kk - kmax) : 0.f;
+                const float XU = X * eu;
+                const float num = fmaf(XU, vv, nn);
+                const float den = dd + XU;
+                float g = 1.f;
+                float xx = 0.f;
+                if constexpr (MODE == MODE_GATED) g = 1.f + __builtin_amdgcn_exp2f(-kLog2e * (float)gr[i * CW]);
+                if constexpr (MODE == MODE_TIMEMIX) {
+                    xx = (float)gr[i * CW];
+                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
+                }
+                const float yv = num * rcp(den * g);
+                if (i < nval) {
+                    st_stream(Y + base + i * C, (TOut)yv);
+                    if constexpr (MODE == MODE_TIMEMIX) {
+                        if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
+                        if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
+                    }
+                }
+                if constexpr (MODE == MODE_TIMEMIX) xs = (i < nval) ? xx : xs;
+                const float e = (i < nval) ? ew : 1.f;
+                nn = fmaf(e, nn, X * vv);
+                dd = fmaf(e, dd, X);
+            }
+        }
+        fin = St{nn, dd, kmax, 0.f};
+    } else {
+        // exact per-token max-trick
+        St s2 = st;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if (i < nval) {
+                const float kk = (float)kr[i * CW];
+                const float vv = (float)vr[i * CW];
+                float num, den;
+                emit(s2, wc, uc, kk, vv, num, den);
+                float g = 1.f;
+                if constexpr (MODE == MODE_GATED) g = 1.f + ex(-(float)gr[i * CW]);
+                if constexpr (MODE == MODE_TIMEMIX) {
+                    const float xx = (float)gr[i * CW];
+                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
+                    if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
+                    if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
+                    xs = xx;
+                }
+                st_stream(Y + base + i * C, (TOut)(num * rcp(den * g)));
+                absorb(s2, wc, kk, vv);
+            }
+        }
+        fin = s2;
+    }
+    return fin;
+}
+
 // Workgroup = (b, channel tile ct of 64 channels, time tile tt of TW = S * L tokens),
 // blockIdx = tt * (B * nCT) + r with (b, ct) = tile_chain(r), so every tile a workgroup waits
 // for has a lower index and was dispatched earlier.  PREFIX selects where the tile's incoming state
@@ -814,31 +951,12 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const TIn *vr = rows + ((size_t)1 * TW + wv * L) * CW + lane;
     const TIn *gr = rows + ((size_t)2 * TW + wv * L) * CW + lane;
 
-    // Phase B: summary of the wave's tokens from the empty state.  A full wave whose rows come
-    // by 16-byte DMA takes them group by group as they land (wave-uniform choice); lanes past C
-    // then drop their summary (their rows are a copy of channel 0).  Then the wave requests its
+    // Phase B: summary of the wave's tokens from the empty state; then the wave requests its
     // gate rows.
     float kmax;   // the weights' reference key: the largest key (or the first group's, staged)
     bool fast;
     float Xs[L];  // the weights e^{k_i - kmax} of a full wave on the fast path
-    St sum;
-    const bool staged = a.vec16 && wlen == L;
-    if (staged) {
-        sum = wave_summary_staged<TIn, L>(kr, vr, ew, uc, kmax, fast, Xs);
-        if (!cok) {
-            sum = st_empty();
-            fast = false;
-        } else if (!fast) {
-            // outside the linear-space guard: the exact per-token recurrence (all rows landed)
-            sum = st_empty();
-#pragma unroll 1
-            for (int i = 0; i < L; ++i) absorb(sum, wc, (float)kr[i * CW], (float)vr[i * CW]);
-        }
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-        __builtin_amdgcn_wave_barrier();
-        sum = wave_summary<TIn, L>(kr, vr, nval, wc, uc, ew, kmax, fast, Xs);
-    }
+    const St sum = summarize_wave<TIn, L>(kr, vr, wlen, nval, cok, a.vec16 != 0, wc, uc, ew, kmax, fast, Xs);
     if constexpr (NT == 3)  // waited for before the emit
         stage_rows<TIn, 1, L>(src + 2, rows + (size_t)2 * TW * CW, TW, wv, lane, b, a.T, C, ct, tile_t0, t0, cs,
                               a.vec16 != 0);
@@ -906,101 +1024,12 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
 
     // Phase E: emit y for the wave's tokens, starting from st.
     __builtin_amdgcn_s_setprio(0);
-    TOut *Y = static_cast<TOut *>(a.y);
-    TIn *XKO = static_cast<TIn *>(a.xk_out);
-    TIn *XVO = static_cast<TIn *>(a.xv_out);
     if constexpr (MODE == MODE_TIMEMIX) {
         if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
     }
-    const float pst = st_logmax(st, wc);
-    // the lane's tokens take the linear-space path; a wave whose lanes all do may stage y
-    const bool lane_fast = fast && pst - kmax <= kGuardState && uc >= kGuardBonus && uc <= kGuardBonusMax;
-    const bool wave_fast = __all(lane_fast);  // voted before the lanes diverge
-    St fin;
-    if (lane_fast) {
-        const float s0 = ex(pst - kmax);
-        float nn = st.a * s0, dd = st.b * s0;
-        // rows as wave-uniform pointers plus a 32-bit lane offset
-        const int64_t row0 = (b * a.T + t0) * C + ct * CW;
-        const unsigned Cu = (unsigned)C;
-        // a full wave (all L tokens, all 64 channels in range, every lane on this path) stages y
-        // in its own v rows, dead once v is in registers, and writes 16 bytes per lane: each
-        // lane's store carries other lanes' channels, so no lane may be on the exact path
-        constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
-        const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16 && wave_fast;
-        TOut *ystage = reinterpret_cast<TOut *>(rows + ((size_t)1 * TW + wv * L) * CW);
-        if (nval == L) {
-            const bool mix = (MODE == MODE_TIMEMIX) && (XKO || XVO);
-            TOut *yrow = Y + row0;
-            TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
-#define RWKV_EMIT(STAGE, MIX)                                                                          \
-    emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
-                                                   xkrow, xvrow, ystage, Cu, lane)
-            if constexpr (MODE == MODE_TIMEMIX) {
-                if (stage_y) {
-                    if (mix) RWKV_EMIT(true, true); else RWKV_EMIT(true, false);
-                } else {
-                    if (mix) RWKV_EMIT(false, true); else RWKV_EMIT(false, false);
-                }
-            } else {
-                if (stage_y) RWKV_EMIT(true, false); else RWKV_EMIT(false, false);
-            }
-#undef RWKV_EMIT
-        } else {
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-                const float kk = (float)kr[i * CW], vv = (float)vr[i * CW];
-                const float X = (i < nval) ? ex(kk - kmax) : 0.f;
-                const float XU = X * eu;
-                const float num = fmaf(XU, vv, nn);
-                const float den = dd + XU;
-                float g = 1.f;
-                float xx = 0.f;
-                if constexpr (MODE == MODE_GATED) g = 1.f + __builtin_amdgcn_exp2f(-kLog2e * (float)gr[i * CW]);
-                if constexpr (MODE == MODE_TIMEMIX) {
-                    xx = (float)gr[i * CW];
-                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
-                }
-                const float yv = num * rcp(den * g);
-                if (i < nval) {
-                    st_stream(Y + base + i * C, (TOut)yv);
-                    if constexpr (MODE == MODE_TIMEMIX) {
-                        if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
-                        if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
-                    }
-                }
-                if constexpr (MODE == MODE_TIMEMIX) xs = (i < nval) ? xx : xs;
-                const float e = (i < nval) ? ew : 1.f;
-                nn = fmaf(e, nn, X * vv);
-                dd = fmaf(e, dd, X);
-            }
-        }
-        fin = St{nn, dd, kmax, 0.f};
-    } else {
-        // exact per-token max-trick
-        St s2 = st;
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-            if (i < nval) {
-                const float kk = (float)kr[i * CW];
-                const float vv = (float)vr[i * CW];
-                float num, den;
-                emit(s2, wc, uc, kk, vv, num, den);
-                float g = 1.f;
-                if constexpr (MODE == MODE_GATED) g = 1.f + ex(-(float)gr[i * CW]);
-                if constexpr (MODE == MODE_TIMEMIX) {
-                    const float xx = (float)gr[i * CW];
-                    g = 1.f + __builtin_amdgcn_exp2f(fmaf(ga, xx, gb * xs));
-                    if (XKO) st_stream(XKO + base + i * C, (TIn)fmaf(mk, xx - xs, xs));
-                    if (XVO) st_stream(XVO + base + i * C, (TIn)fmaf(mv, xx - xs, xs));
-                    xs = xx;
-                }
-                st_stream(Y + base + i * C, (TOut)(num * rcp(den * g)));
-                absorb(s2, wc, kk, vv);
-            }
-        }
-        fin = s2;
-    }
+    const St fin = emit_wave<TIn, TOut, MODE, L>(a, st, Xs, fast, kmax, kr, vr, gr,
+                                                 rows + ((size_t)1 * TW + wv * L) * CW, wc, uc, ew, eu, ga, gb,
+                                                 mk, mv, xs, b, ct, t0, wlen, nval, base, lane);
 
     // A state published into this XCD's L2 is now written through for readers on other XCDs
     // (the outputs above are out of the way).
@@ -1018,6 +1047,225 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
             if (a.x_last) st_stream(static_cast<TIn *>(a.x_last) + b * C + c, (TIn)xs);
         }
     }
+}
+
+// Long tiles: chunk_len CL above the LDS-staged tile length SUBW = S * L (4 waves of L tokens:
+// 128 tokens for 2-byte inputs, 64 for fp32).  A workgroup owns CL tokens of a chain as
+// NSUB = CL / SUBW consecutive sub-tiles that pass one after another through the same LDS rows.
+// Pass 1 folds every sub-tile's wave summaries into the chunk's aggregate, which the tile
+// publishes for the later tiles of its chain (the last tile of a chain, which nothing waits
+// for, skips it); after the look-back, whose words now cover CL tokens each, pass 2 stages
+// each sub-tile again and emits it from the running state, as tile_body does for one tile.
+// The k and v rows are read twice, the second time shortly after the first (so mostly from
+// L2 or the Infinity Cache).  States are published straight to memory (write-through).
+template <typename TIn, typename TOut, int MODE, int L>
+__device__ __forceinline__ void long_tile_body(const ForwardArgs &a, const ChunkWorkspace &ws, int S, int nCT,
+                                               int nTT, int CL, int M, int rot, int G) {
+    constexpr int CW = kTileChannels;
+    constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;  // staged tensors: k, v, [r | x]
+    const int SUBW = S * L;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    TIn *rows = reinterpret_cast<TIn *>(smem);                                          // [NT][SUBW][CW]
+    float *sF = reinterpret_cast<float *>(smem + (size_t)NT * SUBW * CW * sizeof(TIn));  // [4][S][CW]
+
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t BCT = a.B * nCT;
+    const int64_t tt = blockIdx.x / G;
+    const int64_t rem = blockIdx.x - tt * G;
+    if (rem >= BCT) return;
+    __builtin_amdgcn_s_setprio(2);  // pass 1 and the look-back feed the chain's later tiles
+    int64_t b, ct;
+    tile_chain(rem, tt, rot, BCT, nCT, b, ct);
+    const int64_t c = ct * CW + lane;
+    const bool cok = c < a.C;
+    const int64_t C = a.C, BC = a.B * a.C;
+    const int64_t cs = cok ? c : 0;  // loads stay unpredicated: a lane past C reads channel 0
+    const int64_t chunk_t0 = tt * CL;
+    const int64_t chunk_len = std::min<int64_t>(CL, a.T - chunk_t0);
+    const int nsub = (int)((chunk_len + SUBW - 1) / SUBW);
+    const int64_t chain = (b * nCT + ct) * nTT;
+    const bool vec16 = a.vec16 != 0;
+
+    const TIn *K = static_cast<const TIn *>(a.k);
+    const TIn *V = static_cast<const TIn *>(a.v);
+    const TIn *GR = static_cast<const TIn *>(MODE == MODE_GATED ? a.r : a.x);
+    const TIn *src[3] = {K, V, GR};
+
+    const float w_raw = a.w[cs], u_raw = a.u[cs];
+    const float wc = cok ? finite_decay(w_raw) : 0.f;
+    const float uc = cok ? u_raw : 0.f;
+    float mr = 0.f, mk = 0.f, mv = 0.f;
+    if constexpr (MODE == MODE_TIMEMIX) {
+        const float mr_raw = a.mix_r[cs], mk_raw = a.mix_k[cs], mv_raw = a.mix_v[cs];
+        mr = cok ? mr_raw : 0.f;
+        mk = cok ? mk_raw : 0.f;
+        mv = cok ? mv_raw : 0.f;
+    }
+    St prefix = st_empty();
+    if (tt == 0 && a.state_in && cok)
+        prefix = st_load(a.state_in[b * C + c], a.state_in[BC + b * C + c], a.state_in[2 * BC + b * C + c]);
+    asm volatile("" ::: "memory");
+    const float ew = ex(wc), eu = ex(uc);
+    const float ga = -kLog2e * mr, gb = -kLog2e * (1.f - mr);
+    const TIn *kr = rows + ((size_t)0 * SUBW + wv * L) * CW + lane;
+    const TIn *vr = rows + ((size_t)1 * SUBW + wv * L) * CW + lane;
+    const TIn *gr = rows + ((size_t)2 * SUBW + wv * L) * CW + lane;
+
+    const bool anchor = (tt % M) == 0, last = tt == nTT - 1;
+    const bool publishes = nTT > 1 && !last;
+
+    // Pass 1: the chunk's aggregate, from the empty state (only a tile that publishes needs it).
+    // Each wave stages and summarises its own rows; wave S-1 folds the waves' summaries of every
+    // sub-tile in token order.
+    St agg = st_empty();
+    if (publishes) {
+#pragma unroll 1
+        for (int j = 0; j < nsub; ++j) {
+            const int64_t sub_t0 = chunk_t0 + (int64_t)j * SUBW;
+            const int64_t t0 = sub_t0 + (int64_t)wv * L;
+            const int wlen = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - t0));
+            stage_rows<TIn, 2, L>(src, rows, SUBW, wv, lane, b, a.T, C, ct, sub_t0, t0, cs, vec16);
+            float kmax;
+            bool fast;
+            float Xs[L];
+            const St sum = summarize_wave<TIn, L>(kr, vr, wlen, cok ? wlen : 0, cok, vec16, wc, uc, ew, kmax, fast, Xs);
+            sF[(0 * S + wv) * CW + lane] = sum.a;
+            sF[(1 * S + wv) * CW + lane] = sum.b;
+            sF[(2 * S + wv) * CW + lane] = sum.k;
+            sF[(3 * S + wv) * CW + lane] = sum.n;
+            lds_barrier();
+            if (wv == S - 1) {
+                for (int q = 0; q < S; ++q) {
+                    const St sq = St{sF[(0 * S + q) * CW + lane], sF[(1 * S + q) * CW + lane],
+                                     sF[(2 * S + q) * CW + lane], sF[(3 * S + q) * CW + lane]};
+                    const int lq = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - (sub_t0 + (int64_t)q * L)));
+                    agg = combine(agg, sq, (float)lq, wc);
+                }
+            }
+            lds_barrier();  // sF and the rows are rewritten by the next sub-tile
+        }
+        if (wv == S - 1 && !anchor) publish(ws, chain + tt, kAgg, agg, lane, false);
+    }
+
+    // The chunk's incoming state, as tile_body's phase D: INCL(a0) + AGG(a0+1) + ... + AGG(tt-1)
+    // in that fixed order, the polling shared by the waves.
+    if (tt > 0) {
+        const int a0 = (int)(((tt - 1) / M) * M);
+        const int cnt = (int)tt - a0;
+        const int q = (cnt + S - 1) / S;
+        const int lo = a0 + wv * q, hi = std::min(lo + q, (int)tt);
+        St part = st_empty();
+        if (lo < hi) part = fold_published<kMaxAnchorGap / 4>(ws, chain, lo, hi, lo == a0, wc, (float)CL, lane);
+        sF[(0 * S + wv) * CW + lane] = part.a;
+        sF[(1 * S + wv) * CW + lane] = part.b;
+        sF[(2 * S + wv) * CW + lane] = part.k;
+        sF[(3 * S + wv) * CW + lane] = part.n;
+        lds_barrier();
+        for (int j = 0; j < S; ++j) {
+            const int lj = a0 + j * q;
+            if (lj < (int)tt) {
+                const St pj = St{sF[(0 * S + j) * CW + lane], sF[(1 * S + j) * CW + lane],
+                                 sF[(2 * S + j) * CW + lane], sF[(3 * S + j) * CW + lane]};
+                const float span = (float)((int64_t)(std::min(lj + q, (int)tt) - lj) * CL);
+                prefix = (j == 0) ? pj : combine(prefix, pj, span, wc);
+            }
+        }
+        lds_barrier();  // sF is rewritten in pass 2
+    }
+    if (publishes && anchor && wv == S - 1) publish(ws, chain + tt, kIncl, combine(prefix, agg, (float)chunk_len, wc), lane, false);
+
+    // Pass 2: each sub-tile staged again and emitted from the running state.
+    __builtin_amdgcn_s_setprio(0);
+    St running = prefix;
+    float xs = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < nsub; ++j) {
+        const int64_t sub_t0 = chunk_t0 + (int64_t)j * SUBW;
+        const int64_t sub_len = std::min<int64_t>(SUBW, a.T - sub_t0);
+        const int64_t t0 = sub_t0 + (int64_t)wv * L;
+        const int wlen = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - t0));
+        const int nval = cok ? wlen : 0;
+        const int64_t base = (b * a.T + t0) * C + c;
+        if constexpr (MODE == MODE_TIMEMIX) {
+            // wave 0: x[sub_t0 - 1] or x_prev (zeros if absent); later waves read it from LDS
+            if (wv == 0) {
+                const bool from_x = sub_t0 > 0, from_prev = sub_t0 == 0 && a.x_prev != nullptr;
+                const TIn *xsrc = from_prev ? static_cast<const TIn *>(a.x_prev) + b * C + cs
+                                            : GR + (from_x ? (b * a.T + sub_t0 - 1) * C + cs : 0);
+                const float xv = (float)*xsrc;
+                xs = (from_x || from_prev) ? xv : 0.f;
+            }
+            asm volatile("" ::: "memory");
+        }
+        stage_rows<TIn, 2, L>(src, rows, SUBW, wv, lane, b, a.T, C, ct, sub_t0, t0, cs, vec16);
+        float kmax;
+        bool fast;
+        float Xs[L];
+        const St sum = summarize_wave<TIn, L>(kr, vr, wlen, nval, cok, vec16, wc, uc, ew, kmax, fast, Xs);
+        if constexpr (NT == 3)  // waited for before the emit
+            stage_rows<TIn, 1, L>(src + 2, rows + (size_t)2 * SUBW * CW, SUBW, wv, lane, b, a.T, C, ct, sub_t0, t0,
+                                  cs, vec16);
+        sF[(0 * S + wv) * CW + lane] = sum.a;
+        sF[(1 * S + wv) * CW + lane] = sum.b;
+        sF[(2 * S + wv) * CW + lane] = sum.k;
+        sF[(3 * S + wv) * CW + lane] = sum.n;
+        lds_barrier();  // not waiting for the gate rows in flight
+        // every wave folds the waves before it (its exclusive prefix) and all of them (the
+        // sub-tile's aggregate, which carries the running state to the next sub-tile)
+        St excl = st_empty(), sub_agg = st_empty();
+        for (int q = 0; q < S; ++q) {
+            const St sq = St{sF[(0 * S + q) * CW + lane], sF[(1 * S + q) * CW + lane],
+                             sF[(2 * S + q) * CW + lane], sF[(3 * S + q) * CW + lane]};
+            const int lq = (int)std::max<int64_t>(0, std::min<int64_t>(L, a.T - (sub_t0 + (int64_t)q * L)));
+            if (q < wv) excl = combine(excl, sq, (float)lq, wc);
+            sub_agg = combine(sub_agg, sq, (float)lq, wc);
+        }
+        if constexpr (NT == 3) {
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's gate rows have landed,
+            __syncthreads();                // and every other wave's (the time mix reads the previous wave's last x)
+        }
+        const St st = combine(running, excl, (float)std::min<int64_t>((int64_t)wv * L, sub_len), wc);
+        if constexpr (MODE == MODE_TIMEMIX) {
+            if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
+        }
+        // the emit's per-token output offsets (token x C + lane) are the same in every sub-tile;
+        // an opaque copy of the lane index keeps the compiler from hoisting all of them out of
+        // the loop, where they would hold a register each for the whole loop
+        int lane_it = lane;
+        asm volatile("" : "+v"(lane_it));
+        const St fin = emit_wave<TIn, TOut, MODE, L>(a, st, Xs, fast, kmax, kr, vr, gr,
+                                                     rows + ((size_t)1 * SUBW + wv * L) * CW, wc, uc, ew, eu, ga,
+                                                     gb, mk, mv, xs, b, ct, t0, wlen, nval, base, lane_it);
+        running = combine(running, sub_agg, (float)sub_len, wc);
+        // the lane holding token T-1 writes the final state (and x_last)
+        if (nval > 0 && t0 + nval == a.T) {
+            if (a.state_out) {
+                st_stream(a.state_out + b * C + c, fin.a);
+                st_stream(a.state_out + BC + b * C + c, fin.b);
+                st_stream(a.state_out + 2 * BC + b * C + c, st_logmax(fin, wc));
+            }
+            if constexpr (MODE == MODE_TIMEMIX) {
+                if (a.x_last) st_stream(static_cast<TIn *>(a.x_last) + b * C + c, (TIn)xs);
+            }
+        }
+        lds_barrier();  // every wave is done with sF and with the rows it reads of other waves
+    }
+}
+
+// Long tiles of 32-token waves (2-byte inputs, sub-tiles of 128 tokens) and of 16-token waves
+// (fp32 inputs, sub-tiles of 64 tokens).  The sub-tile loop holds more registers than one tile:
+// 32-token waves get up to 168 VGPRs (three waves per SIMD; two for the time mix, 256), 16-token
+// waves up to 128.
+template <typename TIn, typename TOut, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MODE_TIMEMIX ? 2 : 3)))
+    wkv_long32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int CL, int M, int rot, int G) {
+    long_tile_body<TIn, TOut, MODE, 32>(a, ws, S, nCT, nTT, CL, M, rot, G);
+}
+
+template <typename TIn, typename TOut, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+    wkv_long16_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int CL, int M, int rot, int G) {
+    long_tile_body<TIn, TOut, MODE, 16>(a, ws, S, nCT, nTT, CL, M, rot, G);
 }
 
 // 16 tokens per wave (chunk_len = 16 * waves): 96 VGPRs so that five 4-wave workgroups
@@ -1207,11 +1455,41 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     return hipGetLastError();
 }
 
-// 64-token tiles: 4 waves of 16 tokens; 128-token tiles: 4 waves of 32 tokens.
+// Long tiles: chunk_len / (4 L) sub-tiles of 4 waves x L tokens, L = 32 for 2-byte inputs and
+// 16 for fp32 (the staged tile lengths of launch_tile).
+template <typename TIn, typename TOut, int MODE, int L>
+hipError_t launch_long(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    constexpr int S = 4;
+    constexpr int NT = (MODE == MODE_PLAIN) ? 2 : 3;
+    const int nCT = (int)((a.C + kTileChannels - 1) / kTileChannels);
+    const int64_t nTT = (a.T + chunk_len - 1) / chunk_len;
+    const int64_t BCT = a.B * (int64_t)nCT;
+    const int64_t grid = BCT * nTT;
+    if (grid > 0x7fffffff || chunk_len % (S * L) != 0 || BCT > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)NT * S * L * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
+    const void *kern = L == 32 ? reinterpret_cast<const void *>(&wkv_long32_kernel<TIn, TOut, MODE>)
+                               : reinterpret_cast<const void *>(&wkv_long16_kernel<TIn, TOut, MODE>);
+    const int64_t slots = resident_slots(kern, 64 * S, lds);
+    const int rot = (slots > 0 && grid > slots) ? 1 : 0;
+    if constexpr (L == 32)
+        hipLaunchKernelGGL((wkv_long32_kernel<TIn, TOut, MODE>), dim3((unsigned)grid), dim3(64 * S), lds, s, a, ws, S,
+                           nCT, (int)nTT, chunk_len, kMaxAnchorGap, rot, (int)BCT);
+    else
+        hipLaunchKernelGGL((wkv_long16_kernel<TIn, TOut, MODE>), dim3((unsigned)grid), dim3(64 * S), lds, s, a, ws, S,
+                           nCT, (int)nTT, chunk_len, kMaxAnchorGap, rot, (int)BCT);
+    return hipGetLastError();
+}
+
+// 64-token tiles: 4 waves of 16 tokens; 128-token tiles: 4 waves of 32 tokens; longer chunks
+// (up to kMaxChunk) as long tiles of such sub-tiles.
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
-    if constexpr (sizeof(TIn) == 2)
+    if constexpr (sizeof(TIn) == 2) {
         if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
+        if (chunk_len > 128) return launch_long<TIn, TOut, MODE, 32>(a, chunk_len, ws, s);
+    } else {
+        if (chunk_len > 64) return launch_long<TIn, TOut, MODE, 16>(a, chunk_len, ws, s);
+    }
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
 }
 
@@ -1244,11 +1522,9 @@ hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorks
 
 }  // namespace
 
-// Longest tile per dtype: the tile's rows are staged in LDS (64 KB per workgroup).
-int chunk_max_len(int in_2byte, int mode) {
-    (void)mode;
-    return in_2byte ? 128 : 64;
-}
+// Longest tile whose rows are staged in LDS at once (the two-pass scan's granularity); the
+// single-launch scan takes longer chunks as long tiles.
+int tile_max_len(int in_2byte) { return in_2byte ? 128 : 64; }
 
 bool auto_sequential(int64_t B, int64_t T, int64_t C) {
     // Enough independent (b, channel) lanes to fill every SIMD twice over: the

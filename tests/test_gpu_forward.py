@@ -46,16 +46,23 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
 
 
 ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128), ("auto", 0)]
+# chunks longer than the LDS-staged tile (128 tokens for 2-byte inputs, 64 for fp32): long tiles
+LONG = [("chunked", 256), ("chunked", 512), ("chunked", 1024)]
+
+
+def skip_unsupported(in_dt, algo, chunk):
+    if in_dt == "f32" and algo == "two_pass" and chunk > 64:
+        pytest.skip("fp32 inputs: the two-pass scan takes tiles of at most 64 tokens (LDS budget)")
 
 
 # ----------------------------------------------------------------------------- small, ragged
 
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("f32", "f16")])
-@pytest.mark.parametrize("algo,chunk", ALGOS)
+@pytest.mark.parametrize("algo,chunk", ALGOS + LONG)
 def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
-    # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64
-    if in_dt == "f32" and chunk > 64:
-        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
+    # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64.
+    # With chunks of 256 or 512 the last tile is partial (a partial sub-tile); 1024 is one tile.
+    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(2, 1000, 200, seed=41, in_dtype=in_dt, out_dtype=out_dt, gated=True, prior=True)
     ref = oracle_forward(("ragged", in_dt), case)
     y, st = run(case, algo, chunk, label="ragged")
@@ -209,7 +216,8 @@ def test_wide_key_spread_2byte_staged(in_dt):
         check_state(s, ref, f"spread {in_dt} {algo}/{chunk}")
 
 
-GUARD_ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)]
+GUARD_ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128),
+               ("chunked", 256)]
 
 
 @pytest.mark.parametrize("in_dt", ["f32", "f16"])
@@ -218,8 +226,7 @@ def test_bonus_outside_the_linear_space_guard(in_dt, algo, chunk):
     """Channels with u = -25 (below the fast path's bonus guard: the current token's weight would
     underflow against the others) and u = +40 (above it: e^u times a weight of up to e^40
     overflows fp32) take the exact per-token recurrence; their neighbours stay on the fast path."""
-    if in_dt == "f32" and chunk > 64:
-        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
+    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(2, 1000, 192, seed=54, in_dtype=in_dt, out_dtype="f32", gated=True, prior=True)
     u = case["u"].copy()
     u[0::5] = -25.0
@@ -238,8 +245,7 @@ def test_incoming_state_outside_the_linear_space_guard(in_dt, algo, chunk):
     keeps a log-scale near 70 - 0.0067 n for thousands of tokens, so the waves of later tiles
     start more than 60 nats above their own largest key (the incoming-state guard) and take the
     exact recurrence, until the scale has decayed back inside the guard (after ~1000 tokens)."""
-    if in_dt == "f32" and chunk > 64:
-        pytest.skip("fp32 inputs: tiles of at most 64 tokens (LDS budget)")
+    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(1, 2048, 128, seed=55, in_dtype=in_dt, out_dtype="f32", prior=False)
     k = case["k"].astype(np.float64)
     k[0, 5, 0:8] = 70.0
@@ -285,7 +291,7 @@ def test_chain_order_across_xcds(B, T, C, algo, chunk):
 
 
 @pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("two_pass", 64), ("chunked", 128), ("two_pass", 128),
-                                        ("auto", 0)])
+                                        ("auto", 0), ("chunked", 512)])
 def test_deterministic(algo, chunk):
     """Two runs give bitwise equal outputs and states (the look-back folds its predecessors in a
     fixed order whatever the timing); auto takes the 128-token single pass that the fp16
@@ -330,7 +336,7 @@ def test_negative_controls_fail_the_gate():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[1] <= 64])
+@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[0] != "two_pass" or a[1] <= 64] + LONG)
 def test_workload_169m_fp32(algo, chunk):
     """B1 T1024 C768, fp32 k, v ~ N(0,1), empty state, y = wkv (fp32): bar 1e-5."""
     case = wi.workload_inputs(0)
@@ -340,7 +346,7 @@ def test_workload_169m_fp32(algo, chunk):
     check_state(st, ref, f"169m fp32 {algo}/{chunk}")
 
 
-@pytest.mark.parametrize("algo,chunk", ALGOS)
+@pytest.mark.parametrize("algo,chunk", ALGOS + LONG)
 def test_workload_169m_batch_f16(algo, chunk):
     """B8 T1024 C768, fp16 k, v, r, random prior state, y = sigmoid(r) wkv (fp16): bar 2e-3."""
     case = wi.workload_inputs(1)

@@ -153,8 +153,8 @@ def test_auto_forward_under_capture_takes_two_pass():
 
 
 def test_capture_refuses_what_cannot_replay():
-    """On a capturing stream the single-launch chunked scan and the library-cached workspace are
-    refused before anything is enqueued; a call whose T fits in one tile needs neither and is
+    """On a capturing stream the single-launch chunked scan (explicit, or a chunk_len above 128,
+    which only it runs) and the library-cached workspace are refused before anything is enqueued; a call whose T fits in one tile needs neither and is
     captured as it is."""
     import rwkv_wkv_linear_amd as rw
     t = torch()
@@ -173,7 +173,8 @@ def test_capture_refuses_what_cannot_replay():
     note("capture refusals")
     with t.cuda.stream(side):
         with t.cuda.graph(graph):
-            for kw in (dict(algo="chunked", workspace=ws), dict(algo="auto"), dict(algo="two_pass")):
+            for kw in (dict(algo="chunked", workspace=ws), dict(algo="auto"), dict(algo="two_pass"),
+                       dict(algo="auto", chunk_len=256, workspace=ws)):
                 try:
                     rw.rwkv4_wkv_forward(d["k"], d["v"], d["w"], d["u"], y=y, state_in=d["state_in"], r=d["r"], **kw)
                 except rw.RwkvError as e:
@@ -182,7 +183,8 @@ def test_capture_refuses_what_cannot_replay():
                                  chunk_len=128)
     t.cuda.current_stream().wait_stream(side)
     t.cuda.synchronize()
-    assert refused == [("chunked", rw.RWKV_ERR_ARG), ("auto", rw.RWKV_ERR_ARG), ("two_pass", rw.RWKV_ERR_ARG)], refused
+    assert refused == [("chunked", rw.RWKV_ERR_ARG), ("auto", rw.RWKV_ERR_ARG), ("two_pass", rw.RWKV_ERR_ARG),
+                       ("auto", rw.RWKV_ERR_ARG)], refused
     ys.fill_(float("nan"))
     t.cuda.synchronize()
     graph.replay()

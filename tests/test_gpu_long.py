@@ -1,7 +1,9 @@
 """GPU parity of the chunked scan on the long-sequence workload: B1 T65536 C2048,
-fp16 k ~ N(0, 2), v ~ N(0, 1), fp32 output and final state, chunk length swept
-64..1024, checked element by element against the fp64 oracle's recurrence, which
-is itself checked against the direct sums at sampled points."""
+fp16 k ~ N(0, 2), v ~ N(0, 1), fp32 output and final state, chunk length swept over
+64, 128, 256, 512 and 1024 tokens and the automatic choice (128), checked element by
+element against the fp64 oracle's recurrence, which is itself checked against the
+direct sums at sampled points.  Chunks above 128 tokens run as long tiles (128-token
+sub-tiles read twice), and every chain has more than 16 tiles, so anchors are used."""
 import numpy as np
 import pytest
 
@@ -29,7 +31,7 @@ def inputs():
     return _cache["case"], _cache["ref"], _cache["dev"]
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 0])
+@pytest.mark.parametrize("chunk", [64, 128, 256, 512, 1024, 0])
 def test_long_sequence_chunk_sweep(chunk):
     import rwkv_wkv_linear_amd as rw
     t = torch()

@@ -19,6 +19,7 @@ import wkv_inputs as wi
 from gpu_util import TOL, check_output, check_state, host, note, to_dev, tol_for, torch
 
 LDS_PER_CU = 160 * 1024
+_cache = {}
 
 
 def assert_past_one_round(B, T, C, chunk, lds_bytes):
@@ -53,6 +54,20 @@ def test_multi_round_gated_prior():
     y, so = forward(case, 128)
     check_output(host(y), ref, TOL["f16"], "multi-round gated", out_dtype="f16")
     check_state(host(so), ref, "multi-round gated")
+
+
+@pytest.mark.parametrize("chunk", [256, 1024])
+def test_multi_round_long_tiles(chunk):
+    """Long tiles (chunks of 256 or 1024 tokens, 128-token sub-tiles) past one resident round, with
+    anchors (chains of 79 and 20 tiles) and a ragged last tile."""
+    case = wi.forward_case(2, 20000, 2048, seed=86, in_dtype="f16", gated=True, prior=True)
+    assert_past_one_round(2, 20000, 2048, chunk, 3 * 128 * 64 * 2)
+    key = "long tiles"
+    if key not in _cache:
+        _cache[key] = oracle.forward(case)
+    y, so = forward(case, chunk)
+    check_output(host(y), _cache[key], TOL["f16"], f"multi-round long tiles chunk={chunk}", out_dtype="f16")
+    check_state(host(so), _cache[key], f"multi-round long tiles chunk={chunk}")
 
 
 def test_multi_round_bf16_gated_prior():
