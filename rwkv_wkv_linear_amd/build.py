@@ -14,7 +14,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librwkvwkv.so")
-SOURCES = ["wkv_kernels.hip", "mix_kernels.hip", "rwkvwkv_abi.hip"]
+# (source, extra flags, object name): wkv_kernels.hip is compiled once per input dtype
+# (-DRWKV_TU_IN = rwkv_dtype code), so its many kernel instantiations build in parallel
+SOURCES = [("wkv_kernels.hip", ["-DRWKV_TU_IN=0"], "wkv_kernels_f32"),
+           ("wkv_kernels.hip", ["-DRWKV_TU_IN=1"], "wkv_kernels_f16"),
+           ("wkv_kernels.hip", ["-DRWKV_TU_IN=2"], "wkv_kernels_bf16"),
+           ("mix_kernels.hip", [], "mix_kernels"),
+           ("rwkvwkv_abi.hip", [], "rwkvwkv_abi")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",
@@ -57,9 +63,9 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".%s.o" % tag) for s in SOURCES]
-    _run([[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *inc, "-c", os.path.join(CSRC, s), "-o", o]
-          for s, o in zip(SOURCES, objs)], verbose)
+    objs = [os.path.join(objdir, "%s.%s.o" % (name, tag)) for _, _, name in SOURCES]
+    _run([[hipcc(), *HIPCC_FLAGS, *flags, *(extra_flags or []), *inc, "-c", os.path.join(CSRC, src), "-o", o]
+          for (src, flags, _), o in zip(SOURCES, objs)], verbose)
     tmp = LIB + ".tmp" + tag
     try:
         _run([[hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]], verbose)

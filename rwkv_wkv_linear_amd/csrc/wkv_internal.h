@@ -75,6 +75,17 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len);
 void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chunk_len,
                            ChunkWorkspace *ws);
 
+// Per input dtype (the kernels of each are compiled in their own translation unit).
+hipError_t launch_sequential_in0(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_sequential_in1(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_sequential_in2(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_chunked_in0(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+hipError_t launch_chunked_in1(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+hipError_t launch_chunked_in2(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+hipError_t launch_chunked_2pass_in0(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+hipError_t launch_chunked_2pass_in1(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+hipError_t launch_chunked_2pass_in2(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s);
+
 hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s);
 hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
                           hipStream_t s);

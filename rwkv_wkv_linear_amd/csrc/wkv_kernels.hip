@@ -39,6 +39,10 @@
 #include "rwkvwkv.h"
 #include "wkv_internal.h"
 
+#ifndef RWKV_TU_IN
+#error "compile with -DRWKV_TU_IN=0, 1 or 2 (the input dtype of this unit)"
+#endif
+
 #include <algorithm>
 #include <mutex>
 #include <vector>
@@ -1500,28 +1504,48 @@ hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorks
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
 }
 
-// Every (input dtype, output dtype, mode) instantiation; rwkv_dtype codes 0 fp32, 1 fp16, 2 bf16.
-#define RWKV_DISPATCH_MODE(LAUNCH, TI, TO, ...)                                      \
+// This translation unit instantiates the kernels of one input dtype, RWKV_TU_IN (rwkv_dtype
+// code: 0 fp32, 1 fp16, 2 bf16); the build compiles the file once per input dtype, in parallel.
+#if RWKV_TU_IN == 0
+using TuIn = float;
+#elif RWKV_TU_IN == 1
+using TuIn = _Float16;
+#else
+using TuIn = __bf16;
+#endif
+
+// Every (output dtype, mode) instantiation for this unit's input dtype.
+#define RWKV_DISPATCH_MODE(LAUNCH, TO, ...)                                          \
     do {                                                                             \
-        if (a.mode == MODE_PLAIN) return LAUNCH<TI, TO, MODE_PLAIN>(__VA_ARGS__);   \
-        if (a.mode == MODE_GATED) return LAUNCH<TI, TO, MODE_GATED>(__VA_ARGS__);   \
-        return LAUNCH<TI, TO, MODE_TIMEMIX>(__VA_ARGS__);                            \
-    } while (0)
-#define RWKV_DISPATCH_OUT(LAUNCH, TI, ...)                                           \
-    do {                                                                             \
-        if (a.out_dt == 1) RWKV_DISPATCH_MODE(LAUNCH, TI, _Float16, __VA_ARGS__);    \
-        if (a.out_dt == 2) RWKV_DISPATCH_MODE(LAUNCH, TI, __bf16, __VA_ARGS__);      \
-        RWKV_DISPATCH_MODE(LAUNCH, TI, float, __VA_ARGS__);                          \
+        if (a.mode == MODE_PLAIN) return LAUNCH<TuIn, TO, MODE_PLAIN>(__VA_ARGS__); \
+        if (a.mode == MODE_GATED) return LAUNCH<TuIn, TO, MODE_GATED>(__VA_ARGS__); \
+        return LAUNCH<TuIn, TO, MODE_TIMEMIX>(__VA_ARGS__);                          \
     } while (0)
 #define RWKV_DISPATCH(LAUNCH, ...)                                                   \
     do {                                                                             \
-        if (a.in_dt == 1) RWKV_DISPATCH_OUT(LAUNCH, _Float16, __VA_ARGS__);          \
-        if (a.in_dt == 2) RWKV_DISPATCH_OUT(LAUNCH, __bf16, __VA_ARGS__);            \
-        RWKV_DISPATCH_OUT(LAUNCH, float, __VA_ARGS__);                               \
+        if (a.out_dt == 1) RWKV_DISPATCH_MODE(LAUNCH, _Float16, __VA_ARGS__);        \
+        if (a.out_dt == 2) RWKV_DISPATCH_MODE(LAUNCH, __bf16, __VA_ARGS__);          \
+        RWKV_DISPATCH_MODE(LAUNCH, float, __VA_ARGS__);                              \
     } while (0)
 
 }  // namespace
 
+#define RWKV_TU_NAME2(f, k) f##_in##k
+#define RWKV_TU_NAME1(f, k) RWKV_TU_NAME2(f, k)
+#define RWKV_TU_NAME(f) RWKV_TU_NAME1(f, RWKV_TU_IN)
+
+hipError_t RWKV_TU_NAME(launch_sequential)(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATCH(launch_seq_t, a, s); }
+
+hipError_t RWKV_TU_NAME(launch_chunked)(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    RWKV_DISPATCH(launch_chunk_t, a, chunk_len, ws, s);
+}
+
+hipError_t RWKV_TU_NAME(launch_chunked_2pass)(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
+                                             hipStream_t s) {
+    RWKV_DISPATCH(launch_chunk2_t, a, chunk_len, ws, s);
+}
+
+#if RWKV_TU_IN == 0
 // Longest tile whose rows are staged in LDS at once (the two-pass scan's granularity); the
 // single-launch scan takes longer chunks as long tiles.
 int tile_max_len(int in_2byte) { return in_2byte ? 128 : 64; }
@@ -1569,16 +1593,17 @@ void chunk_workspace_carve(void *base, int64_t B, int64_t T, int64_t C, int chun
     ws->aggs = reinterpret_cast<float *>(p + 256 + tiles * 4 * kTileChannels * 8);
 }
 
-hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { RWKV_DISPATCH(launch_seq_t, a, s); }
+#define RWKV_BY_IN(F, ...) \
+    (a.in_dt == 1 ? F##_in1(__VA_ARGS__) : a.in_dt == 2 ? F##_in2(__VA_ARGS__) : F##_in0(__VA_ARGS__))
 
-hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
-                          hipStream_t s) {
-    RWKV_DISPATCH(launch_chunk_t, a, chunk_len, ws, s);
+hipError_t launch_sequential(const ForwardArgs &a, hipStream_t s) { return RWKV_BY_IN(launch_sequential, a, s); }
+
+hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    return RWKV_BY_IN(launch_chunked, a, chunk_len, ws, s);
 }
 
-hipError_t launch_chunked_2pass(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
-                                hipStream_t s) {
-    RWKV_DISPATCH(launch_chunk2_t, a, chunk_len, ws, s);
+hipError_t launch_chunked_2pass(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    return RWKV_BY_IN(launch_chunked_2pass, a, chunk_len, ws, s);
 }
 
 hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s) {
@@ -1593,5 +1618,6 @@ hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((wkv_passthrough_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
+#endif  // RWKV_TU_IN == 0
 
 }  // namespace rwkvwkv
