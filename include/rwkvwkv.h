@@ -198,6 +198,32 @@ rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C,
                                 hipStream_t stream, const rwkv4_opts *opts);
 
 /*
+ * rwkv4_timemix_fused for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * rwkv4_timemix_fused; it calls no hipMalloc or hipFree and no allocating routine.  Instead of a
+ * workspace it uses a 16 MiB scratch array that the library holds in every GPU's memory until
+ * the process ends (its address on a device is looked up on the first call there).  It runs the
+ * sequential kernel (AUTO on large B*C, or RWKV_ALGO_SEQUENTIAL) or the two-pass scan, whose
+ * launches neither wait for one another nor depend on the host, so calls may be captured; the
+ * scratch holds the tile aggregates, 16 bytes per channel and tile, so a call may have at most
+ * B * ceil(C / 64) * ceil(T / chunk_len) = 16384 tiles (B1 T65536 C2048 with 128-token
+ * chunks; B1 T1024 C5120 needs 640), else RWKV_ERR_ARG.
+ *   opts->workspace must be NULL and opts->algo must not be RWKV_ALGO_CHUNKED (RWKV_ERR_ARG);
+ *   chunk_len is the two-pass scan's (at most 128 for 2-byte inputs, 64 for fp32).
+ * Every call on a GPU shares that GPU's scratch, and nothing in it needs clearing (each call
+ * writes the aggregates it reads): calls that may run at the same time on one GPU (different
+ * streams, or graphs replayed concurrently) race on it and must be serialised by the caller.
+ */
+rwkv_status rwkv4_timemix_fused_noalloc(int64_t B, int64_t T, int64_t C,
+                                        const void *x, const void *x_prev, void *x_last,
+                                        const float *mix_k, const float *mix_v, const float *mix_r,
+                                        const void *k, const void *v,
+                                        const float *w, const float *u,
+                                        void *y, void *xk_out, void *xv_out,
+                                        const float *state_in, float *state_out,
+                                        hipStream_t stream, const rwkv4_opts *opts);
+
+/*
  * Pre-LN token-shift prologue of either mixer (the "RWKV-4 14B" page, Facts table: a LayerNorm
  * before each mixer, ln1 before time mixing and ln2 before channel mixing; the port report's
  * Abstract: pre-LN and the token shift that mixes the current and previous token).  Per batch

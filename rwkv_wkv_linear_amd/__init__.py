@@ -67,6 +67,8 @@ def _load():
     lib.rwkv4_timemix_fused.argtypes = [i64, i64, i64, vp, vp, vp, fp, fp, fp, vp, vp, fp, fp, vp, vp, vp,
                                         fp, fp, vp, ctypes.POINTER(Opts)]
     lib.rwkv4_timemix_fused.restype = ctypes.c_int
+    lib.rwkv4_timemix_fused_noalloc.argtypes = lib.rwkv4_timemix_fused.argtypes
+    lib.rwkv4_timemix_fused_noalloc.restype = ctypes.c_int
     lib.rwkv4_shift_mix.argtypes = [i64, i64, i64, vp, vp, vp, fp, fp, ctypes.c_float, fp, fp, fp, vp, vp, vp,
                                     ctypes.c_int, vp]
     lib.rwkv4_shift_mix.restype = ctypes.c_int
@@ -249,7 +251,8 @@ def rwkv4_wkv_step(k, v, r, w, u, state, y=None, *, out_dtype=None, stream=None)
 
 def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, xk_out=None,
                         xv_out=None, x_last=None, state_in=None, state_out=None, out_dtype=None,
-                        chunk_len=0, algo="auto", workspace=None, publish="auto", stream=None):
+                        chunk_len=0, algo="auto", workspace=None, publish="auto", stream=None,
+                        _entry="rwkv4_timemix_fused"):
     """Token shift + WKV + receptance gate: y = sigmoid(xr) * WKV(k, v).
     x, k, v [B, T, C]; x_prev, x_last [B, C] (x's dtype); mix_* [C] float32."""
     torch = _torch()
@@ -274,11 +277,21 @@ def rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, *, x
     _need(workspace, "workspace", device=dev)
     o = _opts(_dtype_code(dt), _dtype_code(odt), None, chunk_len, algo, workspace, publish)
     with torch.cuda.device(dev):
-        _check(_get_lib().rwkv4_timemix_fused(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(mix_k),
+        _check(getattr(_get_lib(), _entry)(B, T, C, _ptr(x), _ptr(x_prev), _ptr(x_last), _ptr(mix_k),
                                        _ptr(mix_v), _ptr(mix_r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                        _ptr(y), _ptr(xk_out), _ptr(xv_out), _ptr(state_in),
                                        _ptr(state_out), _stream(stream, dev), ctypes.byref(o)))
     return y
+
+
+def rwkv4_timemix_fused_noalloc(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y=None, **kw):
+    """rwkv4_timemix_fused on the library's static scratch (no device allocation; no workspace
+    argument; the sequential kernel or the two-pass scan).  The caller passes y (and every other
+    output it wants) when it cannot allocate either."""
+    if kw.get("workspace") is not None:
+        raise ValueError("rwkv4_timemix_fused_noalloc takes no workspace")
+    return rwkv4_timemix_fused(x, x_prev, mix_k, mix_v, mix_r, k, v, w, u, y, _entry="rwkv4_timemix_fused_noalloc",
+                               **kw)
 
 
 def rwkv4_lookback_status(workspace=None, *, stream=None, device=None):
@@ -348,5 +361,5 @@ __all__ = [
     "lib", "LIB_PATH", "Opts", "RwkvError", "header_functions", "status_string",
     "rwkv4_wkv_forward", "rwkv4_wkv_step", "rwkv4_timemix_fused", "rwkv_status_string",
     "rwkv_last_error", "rwkv4_workspace_bytes", "rwkv_abi_version", "rwkv4_shift_mix",
-    "rwkv4_channelmix_gate", "rwkv4_lookback_status",
+    "rwkv4_channelmix_gate", "rwkv4_lookback_status", "rwkv4_timemix_fused_noalloc",
 ]

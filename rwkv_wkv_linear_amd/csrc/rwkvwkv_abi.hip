@@ -93,6 +93,35 @@ rwkv_status cached_workspace(size_t need, hipStream_t stream, void **out) {
     return RWKV_OK;
 }
 
+// Scratch of rwkv4_timemix_fused_noalloc, for callers that cannot allocate: the two-pass scan's
+// tile aggregates (16 bytes per channel and tile, 16 MiB in all).  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code the array's name only stands in for
+// the symbol: its device address on each GPU comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is ever handed to a kernel.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+rwkv_status static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(RWKV_ERR_ARG, "device %d: at most %d devices", dev,
+                                                          kMaxScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(RWKV_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RWKV_OK;
+}
+
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool overlap(const void *p, size_t pn, const void *q, size_t qn) {
@@ -118,6 +147,7 @@ struct Resolved {
     void *workspace = nullptr;
     size_t workspace_bytes = 0;
     int32_t publish = RWKV_PUBLISH_AUTO;
+    bool static_scratch = false;  // rwkv4_timemix_fused_noalloc: the two-pass scan on the static scratch
 };
 
 rwkv_status resolve_opts(const rwkv4_opts *o, Resolved *r) {
@@ -215,10 +245,16 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
     const int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, ei == 2);
     const int tmax = tile_max_len(ei == 2);
     const int64_t nTT = (T + chunk - 1) / chunk;
-    bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
+    bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || o.static_scratch ||
+                    (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
     if (two_pass && chunk > tmax)
         return fail(RWKV_ERR_ARG, "the two-pass scan takes chunk_len up to %d for this input dtype (got %d); longer "
                                   "chunks run in the single-launch scan", tmax, chunk);
+    const int64_t tiles = B * ((C + kTileChannels - 1) / kTileChannels) * nTT;
+    if (T > chunk && o.static_scratch && (size_t)tiles * kTileChannels * 16 > kStaticScratchBytes)
+        return fail(RWKV_ERR_ARG, "%lld tiles need %zu bytes of scratch, more than the %zu this entry point holds "
+                                  "(use the allocating entry point)", (long long)tiles,
+                    (size_t)tiles * kTileChannels * 16, kStaticScratchBytes);
     if (T > chunk && o.workspace) {
         const size_t need = chunk_workspace_bytes(B, T, C, chunk);
         if (o.workspace_bytes < need)
@@ -238,14 +274,19 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
                 return fail(RWKV_ERR_ARG, "the single-launch chunked scan (RWKV_ALGO_CHUNKED, or a chunk_len above "
                                           "%d) cannot be captured into a graph: its look-back is stamped per "
                                           "launch", tmax);
-            if (!o.workspace)
+            if (!o.workspace && !o.static_scratch)
                 return fail(RWKV_ERR_ARG, "a chunked scan under stream capture needs opts->workspace "
                                           "(the library-cached workspace is allocated on first use)");
             two_pass = true;
         }
     }
     ChunkWorkspace ws{};
-    if (T > chunk) {  // more than one tile per chain: the prefixes need scratch
+    if (T > chunk && o.static_scratch) {  // the two-pass scan's aggregates only
+        void *base = nullptr;
+        rwkv_status s = static_scratch(&base);
+        if (s != RWKV_OK) return s;
+        ws.aggs = static_cast<float *>(base);
+    } else if (T > chunk) {  // more than one tile per chain: the prefixes need scratch
         const size_t need = chunk_workspace_bytes(B, T, C, chunk);
         void *base = o.workspace;  // its size was checked above
         if (!base) {
@@ -315,15 +356,14 @@ rwkv_status rwkv4_wkv_step(int64_t B, int64_t C, const float *w, const float *u,
     return run_forward(a, o, stream);
 }
 
-rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,
-                                void *x_last, const float *mix_k, const float *mix_v,
-                                const float *mix_r, const void *k, const void *v, const float *w,
-                                const float *u, void *y, void *xk_out, void *xv_out,
-                                const float *state_in, float *state_out, hipStream_t stream,
-                                const rwkv4_opts *opts) {
-    Resolved o;
-    rwkv_status s = resolve_opts(opts, &o);
-    if (s != RWKV_OK) return s;
+}  // extern "C"
+
+namespace {
+
+rwkv_status timemix_impl(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev, void *x_last,
+                         const float *mix_k, const float *mix_v, const float *mix_r, const void *k, const void *v,
+                         const float *w, const float *u, void *y, void *xk_out, void *xv_out,
+                         const float *state_in, float *state_out, hipStream_t stream, const Resolved &o) {
     if (o.r) return fail(RWKV_ERR_ARG, "opts->r must be NULL for rwkv4_timemix_fused (r is the mixed x)");
     if (T > 0 && !x) return fail(RWKV_ERR_ARG, "x is required when T > 0");
     if (!mix_r) return fail(RWKV_ERR_ARG, "mix_r is required");
@@ -356,6 +396,43 @@ rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C, const void *x, 
     a.state_out = state_out;
     a.mode = MODE_TIMEMIX;
     return run_forward(a, o, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,
+                                void *x_last, const float *mix_k, const float *mix_v,
+                                const float *mix_r, const void *k, const void *v, const float *w,
+                                const float *u, void *y, void *xk_out, void *xv_out,
+                                const float *state_in, float *state_out, hipStream_t stream,
+                                const rwkv4_opts *opts) {
+    Resolved o;
+    rwkv_status s = resolve_opts(opts, &o);
+    if (s != RWKV_OK) return s;
+    return timemix_impl(B, T, C, x, x_prev, x_last, mix_k, mix_v, mix_r, k, v, w, u, y, xk_out, xv_out, state_in,
+                        state_out, stream, o);
+}
+
+rwkv_status rwkv4_timemix_fused_noalloc(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,
+                                        void *x_last, const float *mix_k, const float *mix_v,
+                                        const float *mix_r, const void *k, const void *v, const float *w,
+                                        const float *u, void *y, void *xk_out, void *xv_out,
+                                        const float *state_in, float *state_out, hipStream_t stream,
+                                        const rwkv4_opts *opts) {
+    Resolved o;
+    rwkv_status s = resolve_opts(opts, &o);
+    if (s != RWKV_OK) return s;
+    if (o.workspace)
+        return fail(RWKV_ERR_ARG, "opts->workspace must be NULL: rwkv4_timemix_fused_noalloc uses its own static "
+                                  "scratch");
+    if (o.algo == RWKV_ALGO_CHUNKED)
+        return fail(RWKV_ERR_ARG, "rwkv4_timemix_fused_noalloc runs the sequential kernel or the two-pass scan, "
+                                  "not RWKV_ALGO_CHUNKED");
+    o.static_scratch = true;
+    return timemix_impl(B, T, C, x, x_prev, x_last, mix_k, mix_v, mix_r, k, v, w, u, y, xk_out, xv_out, state_in,
+                        state_out, stream, o);
 }
 
 rwkv_status rwkv4_shift_mix(int64_t B, int64_t T, int64_t C, const void *x, const void *x_prev,

@@ -235,3 +235,22 @@ def test_chunked_workspace_size_checked_before_any_hip_call():
     o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, algo=rw.RWKV_ALGO_TWO_PASS,
              workspace=P + 0x800000, workspace_bytes=255)
     assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "workspace" in rw.rwkv_last_error()
+
+
+def test_noalloc_validation():
+    t = L.rwkv4_timemix_fused_noalloc
+
+    G = 1 << 30  # activations 1 GiB apart, so even the large shape below has no overlap
+
+    def call(B=1, T=8, C=16, o=None):
+        return t(B, T, C, p(1 * G), None, None, p(0x30000), p(0x40000), p(0x50000), p(2 * G), p(3 * G),
+                 p(0x10000), p(0x20000), p(4 * G), None, None, None, None, None,
+                 ctypes.byref(o) if o is not None else None)
+
+    assert call(o=opts(workspace=P + 0x800000, workspace_bytes=1 << 20)) == rw.RWKV_ERR_ARG
+    assert "workspace" in rw.rwkv_last_error()
+    assert call(o=opts(algo=rw.RWKV_ALGO_CHUNKED)) == rw.RWKV_ERR_ARG and "CHUNKED" in rw.rwkv_last_error()
+    # 512 channel tiles x 33 time tiles of 128 tokens: more aggregates than the 16 MiB scratch holds
+    big = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16)
+    assert call(T=4160, C=32768, o=big) == rw.RWKV_ERR_ARG and "scratch" in rw.rwkv_last_error()
+    assert call(B=0) == rw.RWKV_ERR_ARG
