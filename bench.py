@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--workload", default="timemix14b", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "two_pass", "sequential"])
+    ap.add_argument("--publish", default="auto", choices=["auto", "l2_first", "write_through"],
+                    help="how the single-pass scan publishes its look-back states (results are identical)")
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-xkv", action="store_true",
@@ -80,6 +82,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="decode14b: capture the 40 layers' launches into one HIP graph and replay it "
                          "per step")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time the same-pattern bandwidth ceilings (libwkvceiling.so): the workload's "
+                         "bytes moved in its kernel's launch shape and memory instructions with no arithmetic, "
+                         "and a plain grid-stride stream of the same bytes")
     ap.add_argument("--copy-kernel", action="store_true",
                     help="time a plain device-to-device copy instead (counter calibration)")
     ap.add_argument("--copy-mib", type=float, default=256.0)
@@ -181,6 +187,80 @@ def copy_kernel(args):
                       "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
 
 
+# workload -> (pattern, inputs, input bytes, output bytes, tokens per wave, LDS bytes of the scan kernel)
+CEILING_PATTERNS = {
+    "timemix14b": ("tile", 3, 2, 2, 32, 3 * 128 * 64 * 2 + 4 * 4 * 64 * 4),
+    "gated169m": ("tile", 3, 2, 2, 32, 3 * 128 * 64 * 2 + 4 * 4 * 64 * 4),
+    "plain169m": ("tile", 2, 4, 4, 16, 2 * 64 * 64 * 4 + 4 * 4 * 64 * 4),
+    "long": ("tile", 2, 2, 4, 32, 2 * 128 * 64 * 2 + 4 * 4 * 64 * 4),
+    "decode14b": ("lanes", 3, 2, 2, 0, 0),
+}
+
+
+def ceilings(name, su, args, torch, K, W):
+    """Time the same-pattern ceilings of a workload like its kernel: K back-to-back launches
+    between one pair of events on the stream, on rotated buffer sets of >= rotate_gib (one set when
+    a set alone exceeds 1 GiB).  Returns a dict for the JSON line, or None for the mixers."""
+    if name not in CEILING_PATTERNS:
+        return None
+    from rwkv_wkv_linear_amd.build import CEIL_LIB
+    lib = ctypes.CDLL(CEIL_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.wkvceil_tile.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, vp]
+    lib.wkvceil_lanes.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, i64, ctypes.c_int, vp]
+    lib.wkvceil_stream.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, ctypes.c_int, vp]
+    pattern, n_in, ei, eo, L, lds = CEILING_PATTERNS[name]
+    B, T, C = su.B, su.T, su.C
+    E = B * T * C
+    dev = torch.device("cuda:0")
+    hs = vp(su.stream.cuda_stream)
+    state_bytes = 24 * B * C if pattern == "lanes" else 0
+    set_bytes = (n_in * ei + eo) * E + state_bytes
+    R = 1 if set_bytes >= 2**30 else max(2, math.ceil(args.rotate_gib * 2**30 / set_bytes))
+    sets = []
+    for _ in range(R):
+        ins = [torch.empty(E * ei, dtype=torch.uint8, device=dev).random_(0, 60) for _ in range(n_in)]
+        out = torch.empty(E * eo, dtype=torch.uint8, device=dev)
+        st = torch.empty(3 * B * C, dtype=torch.float32, device=dev).normal_() if pattern == "lanes" else None
+        sets.append((ins, out, st))
+
+    def ptrs(ins):
+        return [vp(t.data_ptr()) for t in ins] + [None] * (3 - len(ins))
+
+    def launch(i, kind):
+        ins, out, st = sets[i % R]
+        if kind == "stream":
+            # equal-size inputs and output: the output in the inputs' element size
+            nbytes = E * ei
+            rc = lib.wkvceil_stream(*ptrs(ins), n_in, vp(out.data_ptr()), nbytes, 2048, hs)
+        elif pattern == "tile":
+            rc = lib.wkvceil_tile(*ptrs(ins), n_in, vp(out.data_ptr()), B, T, C, L, ei, eo, lds, hs)
+        else:
+            rc = lib.wkvceil_lanes(*ptrs(ins), n_in, vp(out.data_ptr()), vp(st.data_ptr()), E, ei, hs)
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel {kind}: status {rc}")
+
+    res = {}
+    for kind in ("pattern", "stream"):
+        for i in range(W):
+            launch(i, kind)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(su.stream)
+        for i in range(K):
+            launch(W + i, kind)
+        ev1.record(su.stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / K * 1e3
+        # state_bytes: the fp32 state read and written once each (12 + 12 bytes per (b, c))
+        moved = (n_in * ei + (eo if kind == "pattern" else ei)) * E + (state_bytes if kind == "pattern" else 0)
+        res[kind] = {"kernel_avg_us": us, "GBps": moved / (us * 1e-6) / 1e9, "bytes": moved}
+    return {"pattern": f"{pattern}: {n_in} x {ei}-byte inputs, {eo}-byte output"
+                       + (", fp32 state read and written" if pattern == "lanes" else f", tiles of 4 x {L} tokens"),
+            "same_pattern": res["pattern"], "plain_stream": res["stream"]}
+
+
 class Setup:
     """Device buffers and the raw ctypes calls of one workload."""
 
@@ -220,6 +300,7 @@ class Setup:
         opts.out_dtype = self.act_code if wl.out_dtype == "f16" else rw.RWKV_F32
         opts.chunk_len = args.chunk_len
         opts.algo = {"auto": 0, "sequential": 1, "chunked": 2, "two_pass": 3}[args.algo]
+        opts.publish = {"auto": 0, "l2_first": 1, "write_through": 2}[args.publish]
         self.opts = opts
         self.keep = []
         case = wi.workload_inputs(idx)
@@ -440,7 +521,7 @@ def main():
     achieved = su.launch_bytes / (launch_avg_ms * 1e-3) / 1e9
     # the committed counters describe the default headline launch only
     default_launch = (name == "timemix14b" and not args.with_xkv and not args.bf16 and not args.chunk_len
-                      and args.algo == "auto")
+                      and args.algo == "auto" and args.publish == "auto")
     traffic = counters_traffic() if default_launch else None
     chunk = args.chunk_len if args.chunk_len else None
     result = {
@@ -459,7 +540,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": su.desc, "B": su.B, "T": su.T, "C": su.C, "io_dtype": su.io,
                    "entry_point": su.entry, "launches_per_step": su.launches_per_step,
-                   "algo": args.algo, "chunk_len": chunk, "rotated_sets": len(su.sets),
+                   "algo": args.algo, "chunk_len": chunk, "publish": args.publish, "rotated_sets": len(su.sets),
                    "xk_xv_out": bool(args.with_xkv),
                    "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -482,6 +563,11 @@ def main():
         result["warm_same_buffers"] = {"kernel_avg_us": warm_ms * 1e3,
                                        "achieved_GBps": su.launch_bytes / (warm_ms * 1e-3) / 1e9,
                                        "launches": Kw}
+    if args.ceiling:
+        result["ceiling"] = ceilings(name, su, args, torch, min(K, 200), W)
+        if result["ceiling"]:
+            result["ceiling"]["kernel_over_ceiling"] = (launch_avg_ms * 1e3
+                                                        / result["ceiling"]["same_pattern"]["kernel_avg_us"])
     result["cpu_baseline"] = None if args.no_cpu_baseline else \
         cpu_baseline(name, su.cpu_case, su.cpu_elements, su.cpu_sample)
     if result["cpu_baseline"]:

@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librwkvwkv.so")
+# the benchmark's bandwidth ceilings (stream_ceiling.hip): a library of its own, not linked into
+# librwkvwkv and not part of its ABI
+CEIL_LIB = os.path.join(HERE, "libwkvceiling.so")
 # (source, extra flags, object name): wkv_kernels.hip is compiled once per input dtype
 # (-DRWKV_TU_IN = rwkv_dtype code), so its many kernel instantiations build in parallel
 SOURCES = [("wkv_kernels.hip", ["-DRWKV_TU_IN=0"], "wkv_kernels_f32"),
@@ -67,13 +70,16 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     _run([[hipcc(), *HIPCC_FLAGS, *flags, *(extra_flags or []), *inc, "-c", os.path.join(CSRC, src), "-o", o]
           for (src, flags, _), o in zip(SOURCES, objs)], verbose)
     tmp = LIB + ".tmp" + tag
+    ctmp = CEIL_LIB + ".tmp" + tag
     try:
-        _run([[hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]], verbose)
+        _run([[hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp],
+              [hipcc(), *HIPCC_FLAGS, "-shared", os.path.join(CSRC, "stream_ceiling.hip"), "-o", ctmp]], verbose)
     finally:
         for o in objs:
             if os.path.exists(o):
                 os.remove(o)
     os.replace(tmp, LIB)
+    os.replace(ctmp, CEIL_LIB)
     return LIB
 
 

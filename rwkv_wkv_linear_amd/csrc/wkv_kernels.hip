@@ -600,16 +600,20 @@ __device__ __forceinline__ St wave_summary_staged(const TIn *kr, const TIn *vr, 
 // numerator/denominator (nn, dd, scaled by e^{-kmax}), then the recurrence step.  With
 // P = X v the four updates are single FMAs: num = nn + e^u P, den = dd + e^u X,
 // nn <- e^w nn + P, dd <- e^w dd + X.  The optional writes are template switches so the
-// unrolled loop has no branches: STAGE puts y in the wave's LDS v rows (each row is read
-// into registers before it is overwritten) and writes every finished batch of rows with
-// 16-byte stores (yrow 16-byte aligned, all 64 channels in range), MIX
+// unrolled loop has no branches: STAGE puts y in LDS, rows [0, L/2) at ystage_lo and rows
+// [L/2, L) at ystage_hi, and writes every finished batch of rows with 16-byte stores (yrow
+// 16-byte aligned, all 64 channels in range).  The staging rows are the wave's dead k rows and
+// its v rows; a v row is read into registers at the start of its batch, before any y row that
+// overlaps it is written (an output twice the input's size covers input rows 2(i - L/2) and
+// 2(i - L/2) + 1 with output row i >= L/2, all at or before i).  MIX
 // writes the time-mix xk/xv rows.  Xs holds the weights e^{k_i - kmax} from the summary
 // phase; vr, gr point at the lane's first staged row.  The gate factor is 1 + e^{-r_i}
 // (r_i = mr x_i + (1 - mr) x_{i-1} for the time mix, in base 2 as ga x_i + gb x_{i-1}).
 template <typename TIn, typename TOut, int MODE, int L, bool STAGE, bool MIX>
 __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, const TIn *gr,
                                           float eu, float ew, float ga, float gb, float mk, float mv, float &xs,
-                                          float &nn, float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage,
+                                          float &nn, float &dd, TOut *yrow, TIn *xkrow, TIn *xvrow, TOut *ystage_lo,
+                                          TOut *ystage_hi,
                                           unsigned Cu, int lane) {
     constexpr int CW = kTileChannels;
     constexpr int LB = 8;  // rows read from LDS per batch, to bound the registers they occupy
@@ -647,7 +651,7 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
             }
             const TOut yv = (TOut)(num * rcp(dg));
             if constexpr (STAGE)
-                ystage[i * CW + lane] = yv;
+                (i < L / 2 ? ystage_lo + i * CW : ystage_hi + (i - L / 2) * CW)[lane] = yv;
             else
                 st_stream(yrow + i * Cu + (unsigned)lane, yv);
             nn = fmaf(ew, nn, P);
@@ -665,7 +669,8 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
 #pragma unroll
             for (int j = 0; j < LB / RPI; ++j) {
                 const int r = h + j * RPI + rs;
-                const f4 chunk = *reinterpret_cast<const f4 *>(ystage + r * CW + q * CH16);
+                const TOut *ys = h < L / 2 ? ystage_lo + r * CW : ystage_hi + (r - L / 2) * CW;
+                const f4 chunk = *reinterpret_cast<const f4 *>(ys + q * CH16);
                 st_stream(reinterpret_cast<f4 *>(yrow + r * Cu + q * CH16), chunk);
             }
         }
@@ -704,12 +709,13 @@ __device__ __forceinline__ St summarize_wave(const TIn *kr, const TIn *vr, int w
 
 // Phase E of a tile: emit y (and the time mix's xk, xv) for the wave's tokens starting from the
 // state st, and return the state after them.  kr, vr, gr point at the lane's first staged key,
-// value and gate row, vrow0 at the wave's first v row (y is staged there); Xs holds the weights
+// value and gate row, krow0 and vrow0 at the wave's first k and v rows (y is staged there); Xs holds the weights
 // of the linear-space summary (fast), kmax their reference key; xs is the time mix's previous
 // token, updated to the wave's last.  base is the element offset of the lane's first token.
 template <typename TIn, typename TOut, int MODE, int L>
 __device__ __forceinline__ St emit_wave(const ForwardArgs &a, const St &st, const float (&Xs)[L], bool fast,
-                                        float kmax, const TIn *kr, const TIn *vr, const TIn *gr, TIn *vrow0,
+                                        float kmax, const TIn *kr, const TIn *vr, const TIn *gr, TIn *krow0,
+                                        TIn *vrow0,
                                         float wc, float uc, float ew, float eu, float ga, float gb, float mk,
                                         float mv, float &xs, int64_t b, int64_t ct, int64_t t0, int wlen, int nval,
                                         int64_t base, int lane) {
@@ -730,18 +736,20 @@ __device__ __forceinline__ St emit_wave(const ForwardArgs &a, const St &st, cons
         const int64_t row0 = (b * a.T + t0) * C + ct * CW;
         const unsigned Cu = (unsigned)C;
         // a full wave (all L tokens, all 64 channels in range, every lane on this path) stages y
-        // in its own v rows, dead once v is in registers, and writes 16 bytes per lane: each
-        // lane's store carries other lanes' channels, so no lane may be on the exact path
-        constexpr bool kStageFits = sizeof(TOut) <= sizeof(TIn);
+        // in LDS and writes 16 bytes per lane: each lane's store carries other lanes' channels,
+        // so no lane may be on the exact path.  y rows up to the input's size go in the wave's v
+        // rows, dead once read; twice that size in its k rows (first half) and v rows
+        constexpr bool kStageFits = sizeof(TOut) <= 2 * sizeof(TIn);
         const bool stage_y = kStageFits && wlen == L && ct * CW + CW <= C && a.vec16y && a.vec16 && wave_fast;
-        TOut *ystage = reinterpret_cast<TOut *>(vrow0);
+        TOut *ystage_lo = reinterpret_cast<TOut *>(sizeof(TOut) > sizeof(TIn) ? krow0 : vrow0);
+        TOut *ystage_hi = sizeof(TOut) > sizeof(TIn) ? reinterpret_cast<TOut *>(vrow0) : ystage_lo + (L / 2) * CW;
         if (nval == L) {
             const bool mix = (MODE == MODE_TIMEMIX) && (XKO || XVO);
             TOut *yrow = Y + row0;
             TIn *xkrow = XKO ? XKO + row0 : nullptr, *xvrow = XVO ? XVO + row0 : nullptr;
 #define RWKV_EMIT(STAGE, MIX)                                                                          \
     emit_full<TIn, TOut, MODE, L, STAGE, MIX>(Xs, vr, gr, eu, ew, ga, gb, mk, mv, xs, nn, dd, yrow, \
-                                                   xkrow, xvrow, ystage, Cu, lane)
+                                                   xkrow, xvrow, ystage_lo, ystage_hi, Cu, lane)
             if constexpr (MODE == MODE_TIMEMIX) {
                 if (stage_y) {
                     if (mix) RWKV_EMIT(true, true); else RWKV_EMIT(true, false);
@@ -1032,6 +1040,7 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
     }
     const St fin = emit_wave<TIn, TOut, MODE, L>(a, st, Xs, fast, kmax, kr, vr, gr,
+                                                 rows + ((size_t)0 * TW + wv * L) * CW,
                                                  rows + ((size_t)1 * TW + wv * L) * CW, wc, uc, ew, eu, ga, gb,
                                                  mk, mv, xs, b, ct, t0, wlen, nval, base, lane);
 
@@ -1238,6 +1247,7 @@ __device__ __forceinline__ void long_tile_body(const ForwardArgs &a, const Chunk
         int lane_it = lane;
         asm volatile("" : "+v"(lane_it));
         const St fin = emit_wave<TIn, TOut, MODE, L>(a, st, Xs, fast, kmax, kr, vr, gr,
+                                                     rows + ((size_t)0 * SUBW + wv * L) * CW,
                                                      rows + ((size_t)1 * SUBW + wv * L) * CW, wc, uc, ew, eu, ga,
                                                      gb, mk, mv, xs, b, ct, t0, wlen, nval, base, lane_it);
         running = combine(running, sub_agg, (float)sub_len, wc);
