@@ -1430,8 +1430,6 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     const size_t lds = (size_t)NT * chunk_len * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
     if (lds > 65536) return hipErrorInvalidConfiguration;
     if (blocks > 0x7fffffff || S < 1 || 64 * S > 1024) return hipErrorInvalidConfiguration;
-    // an anchor every 16 tiles: a chain of up to 16 tiles has no serial anchor hop at all
-    const int M = kMaxAnchorGap;
     if (S < 4) return hipErrorInvalidConfiguration;  // each wave polls at most 16 / S tiles
     if (PREFIX == PREFIX_AGGS && nTT > 1) {
         // first pass: aggregates of the first nTT - 1 time tiles (k and v rows only)
@@ -1457,6 +1455,12 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     const int64_t G = pad ? Gp : BCT;
     const int64_t grid = G * nTT;
     const int rot = (slots > 0 && grid > slots) ? 1 : 0;  // more than one round of workgroups
+    // Anchor spacing.  Within one round every tile is in flight at once and an anchor every 16
+    // tiles leaves a chain of up to 16 tiles with no serial anchor hop.  Past one round the tiles
+    // of a chain arrive in order; for 128-token tiles an anchor every 8 halves the words each
+    // look-back reads (B1 T65536 C2048: 238.8 -> 234.9 us; every 4: 273 us, the anchors' own
+    // chain too slow), while 64-token tiles, twice as many per chain, keep 16 (308 -> 324 us at 8).
+    const int M = (rot && L == 32) ? kMaxAnchorGap / 2 : kMaxAnchorGap;
     const bool one_xcd = rot == 0 && G % 8 == 0;
     const int lp = PREFIX == PREFIX_LOOKBACK && (a.publish == RWKV_PUBLISH_L2_FIRST ||
                                                  (a.publish == RWKV_PUBLISH_AUTO && one_xcd));
