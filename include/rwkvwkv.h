@@ -115,9 +115,12 @@ typedef struct rwkv4_opts {
     const void *r;           /* rwkv4_wkv_forward only: [B,T,C] receptance, in_dtype;
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
     int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (128
-                                for 2-byte inputs (fp16, bf16), 64 for fp32), else 64 or
-                                128 (2-byte) / 64 (fp32): the tile's rows are staged in
-                                the workgroup's LDS */
+                                for 2-byte inputs (fp16, bf16), 64 for fp32), else a power
+                                of two in [64, 1024].  Up to 128 (2-byte) / 64 (fp32) the
+                                tile's rows are staged in LDS at once; longer tiles (the
+                                single-launch scan only) run as sub-tiles of that length,
+                                read twice (aggregate, then output).  The two-pass scan
+                                takes up to 128 (2-byte) / 64 (fp32): ERR_ARG above. */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per (device,
                                 stream), allocated on first use;
