@@ -116,7 +116,7 @@ typedef struct rwkv4_opts {
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
     int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (128
                                 for 2-byte inputs (fp16, bf16), 64 for fp32), else a power
-                                of two in [64, 1024].  Up to 128 (2-byte) / 64 (fp32) the
+                                of two in [16, 1024].  Up to 128 (2-byte) / 64 (fp32) the
                                 tile's rows are staged in LDS at once; longer tiles (the
                                 single-launch scan only) run as sub-tiles of that length,
                                 read twice (aggregate, then output).  The two-pass scan

@@ -60,7 +60,7 @@ struct ChunkWorkspace {
 };
 
 constexpr int kTileChannels = 64;  // channels per workgroup tile
-constexpr int kMinChunk = 64, kMaxChunk = 1024;
+constexpr int kMinChunk = 16, kMaxChunk = 1024;
 
 // Longest tile whose rows are staged in LDS at once: 128 tokens for 2-byte inputs, 64 for fp32.
 // The two-pass scan takes chunk lengths up to it; the single-launch scan runs longer chunks (up

@@ -58,7 +58,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyP = -1.0e38f;  // p of the empty state (finite, so differences stay defined)
 constexpr uint32_t kAgg = 1u, kIncl = 2u;
 constexpr uint32_t kMaxSpins = 1u << 16;  // tens of milliseconds of polling (one memory round trip per spin) before a look-back gives up
-constexpr int kMaxAnchorGap = 16;         // spacing of anchor tiles in a chain (S >= 4 waves poll <= 4 each)
+constexpr int kMaxAnchorGap = 16;         // largest spacing of anchor tiles in a chain (a wave polls <= 4)
 
 template <typename T> struct Raw;
 template <> struct Raw<float> { using type = f4; };
@@ -665,11 +665,14 @@ __device__ __forceinline__ void emit_full(const float (&Xs)[L], const TIn *vr, c
             constexpr int CHUNKS = CW / CH16;
             constexpr int RPI = 64 / CHUNKS;             // rows per store instruction
             static_assert(LB % RPI == 0, "a batch is a whole number of store instructions");
+            // the halves are apart only for an output wider than the input (RPI 4); the rows of
+            // one store instruction then lie in one half
+            static_assert(sizeof(TOut) <= sizeof(TIn) || (L / 2) % RPI == 0, "one half per store");
             const int q = lane % CHUNKS, rs = lane / CHUNKS;
 #pragma unroll
             for (int j = 0; j < LB / RPI; ++j) {
                 const int r = h + j * RPI + rs;
-                const TOut *ys = h < L / 2 ? ystage_lo + r * CW : ystage_hi + (r - L / 2) * CW;
+                const TOut *ys = h + j * RPI < L / 2 ? ystage_lo + r * CW : ystage_hi + (r - L / 2) * CW;
                 const f4 chunk = *reinterpret_cast<const f4 *>(ys + q * CH16);
                 st_stream(reinterpret_cast<f4 *>(yrow + r * Cu + q * CH16), chunk);
             }
@@ -1290,6 +1293,13 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(5)))
     tile_body<TIn, TOut, MODE, 16, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
 }
 
+// 8 tokens per wave: 32-token tiles of 4 waves, 16-token tiles of 2.
+template <typename TIn, typename TOut, int MODE, int PREFIX>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
+    wkv_tile8_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp, int G) {
+    tile_body<TIn, TOut, MODE, 8, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
+}
+
 // 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
 // quarter of the look-back reads; three 52 KB workgroups share a CU, and with that
 // occupancy each wave may hold its 32 weights in registers.
@@ -1429,8 +1439,7 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     // workgroups per CU (160 KB), 28 KB five.
     const size_t lds = (size_t)NT * chunk_len * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
     if (lds > 65536) return hipErrorInvalidConfiguration;
-    if (blocks > 0x7fffffff || S < 1 || 64 * S > 1024) return hipErrorInvalidConfiguration;
-    if (S < 4) return hipErrorInvalidConfiguration;  // each wave polls at most 16 / S tiles
+    if (blocks > 0x7fffffff || S < 1 || 64 * S > 256) return hipErrorInvalidConfiguration;
     if (PREFIX == PREFIX_AGGS && nTT > 1) {
         // first pass: aggregates of the first nTT - 1 time tiles (k and v rows only)
         const int64_t agg_blocks = a.B * (int64_t)nCT * (nTT - 1);
@@ -1441,8 +1450,9 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const void *kern = L == 32 ? reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>)
-                               : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
+    const void *kern = L == 32  ? reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>)
+                       : L == 8 ? reinterpret_cast<const void *>(&wkv_tile8_kernel<TIn, TOut, MODE, PREFIX>)
+                                : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
     const int64_t slots = resident_slots(kern, 64 * S, lds);
     // States go into the publishing XCD's L2 first when every tile of a chain runs on one XCD:
     // workgroup i runs on XCD i mod 8, tile (tt, chain r) is workgroup tt * G + r with G
@@ -1460,12 +1470,17 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     // of a chain arrive in order; for 128-token tiles an anchor every 8 halves the words each
     // look-back reads (B1 T65536 C2048: 238.8 -> 234.9 us; every 4: 273 us, the anchors' own
     // chain too slow), while 64-token tiles, twice as many per chain, keep 16 (308 -> 324 us at 8).
-    const int M = (rot && L == 32) ? kMaxAnchorGap / 2 : kMaxAnchorGap;
+    // Each wave of a look-back folds at most kMaxAnchorGap / 4 tiles, so a workgroup of fewer
+    // than 4 waves (16-token tiles) anchors every 4 S tiles.
+    const int M = std::min((rot && L == 32) ? kMaxAnchorGap / 2 : kMaxAnchorGap, 4 * S);
     const bool one_xcd = rot == 0 && G % 8 == 0;
     const int lp = PREFIX == PREFIX_LOOKBACK && (a.publish == RWKV_PUBLISH_L2_FIRST ||
                                                  (a.publish == RWKV_PUBLISH_AUTO && one_xcd));
     if constexpr (L == 32)
         hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
+                           a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
+    else if constexpr (L == 8)
+        hipLaunchKernelGGL((wkv_tile8_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
                            a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
     else
         hipLaunchKernelGGL((wkv_tile_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
@@ -1498,10 +1513,12 @@ hipError_t launch_long(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     return hipGetLastError();
 }
 
-// 64-token tiles: 4 waves of 16 tokens; 128-token tiles: 4 waves of 32 tokens; longer chunks
-// (up to kMaxChunk) as long tiles of such sub-tiles.
+// 16- and 32-token tiles: 2 or 4 waves of 8 tokens; 64-token tiles: 4 waves of 16 tokens;
+// 128-token tiles: 4 waves of 32 tokens; longer chunks (up to kMaxChunk) as long tiles of such
+// sub-tiles.
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    if (chunk_len <= 32) return launch_tile<TIn, TOut, MODE, 8, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
     if constexpr (sizeof(TIn) == 2) {
         if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
         if (chunk_len > 128) return launch_long<TIn, TOut, MODE, 32>(a, chunk_len, ws, s);
@@ -1513,6 +1530,7 @@ hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorksp
 
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
+    if (chunk_len <= 32) return launch_tile<TIn, TOut, MODE, 8, PREFIX_AGGS>(a, chunk_len, ws, s);
     if constexpr (sizeof(TIn) == 2)
         if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_AGGS>(a, chunk_len, ws, s);
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
@@ -1579,7 +1597,7 @@ int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_2byte) {
     // the tiles per chain and quarter the look-back reads, and three 52 KB workgroups per CU
     // still hold a layer-sized call at once: 14B layer 18.2 -> 17.3 us, 169m batch 20.6 ->
     // 18.1 us, B1 T65536 C2048 386 -> 286 us.  fp32 rows are twice the size: 64 tokens.
-    return in_2byte ? 2 * kMinChunk : kMinChunk;
+    return in_2byte ? 128 : 64;
 }
 
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t C, int chunk_len) {

@@ -81,7 +81,7 @@ def test_bad_opts():
     assert fwd(o=opts(out_dtype=-1)) == rw.RWKV_ERR_DTYPE
     assert fwd(o=opts(algo=5)) == rw.RWKV_ERR_ARG
     assert fwd(o=opts(algo=4)) == rw.RWKV_ERR_ARG
-    for c in (32, 100, 2048, -64):
+    for c in (8, 48, 100, 2048, -64):
         assert fwd(o=opts(chunk_len=c)) == rw.RWKV_ERR_ARG, c
     assert fwd(o=opts(workspace=P + 4, workspace_bytes=1 << 20)) == rw.RWKV_ERR_ALIGN
     for bad in (-1, 3):

@@ -35,7 +35,8 @@ def run_forward(case, algo, chunk):
     return host(y), host(so)
 
 
-ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 128), ("auto", 0), ("chunked", 512)]
+ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 128), ("auto", 0), ("chunked", 512),
+         ("chunked", 32), ("two_pass", 16)]
 
 
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "bf16"), ("f32", "bf16")])

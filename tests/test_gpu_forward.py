@@ -48,6 +48,8 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
 ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128), ("auto", 0)]
 # chunks longer than the LDS-staged tile (128 tokens for 2-byte inputs, 64 for fp32): long tiles
 LONG = [("chunked", 256), ("chunked", 512), ("chunked", 1024)]
+# chunks shorter than 64 tokens: waves of 8 tokens (4 of them, or 2 with anchors every 8 tiles)
+SHORT = [("chunked", 16), ("chunked", 32), ("two_pass", 16), ("two_pass", 32)]
 
 
 def skip_unsupported(in_dt, algo, chunk):
@@ -58,7 +60,7 @@ def skip_unsupported(in_dt, algo, chunk):
 # ----------------------------------------------------------------------------- small, ragged
 
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("f32", "f16")])
-@pytest.mark.parametrize("algo,chunk", ALGOS + LONG)
+@pytest.mark.parametrize("algo,chunk", ALGOS + LONG + SHORT)
 def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64.
     # With chunks of 256 or 512 the last tile is partial (a partial sub-tile); 1024 is one tile.
@@ -72,7 +74,8 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64),
+                                        ("chunked", 16)])
 def test_odd_channels(C, algo, chunk):
     # C % 4 != 0 takes the per-element path; C < 64 leaves most of a tile masked
     case = wi.forward_case(3, 300, C, seed=42, in_dtype="f16", gated=True, prior=True)
@@ -217,7 +220,7 @@ def test_wide_key_spread_2byte_staged(in_dt):
 
 
 GUARD_ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128),
-               ("chunked", 256)]
+               ("chunked", 256), ("chunked", 16), ("two_pass", 32)]
 
 
 @pytest.mark.parametrize("in_dt", ["f32", "f16"])
@@ -279,7 +282,8 @@ def test_split_sequence_carry(algo):
 
 
 @pytest.mark.parametrize("B,T,C", [(3, 700, 512), (1, 900, 1024)])
-@pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128)])
+@pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128),
+                                        ("chunked", 32)])
 def test_chain_order_across_xcds(B, T, C, algo, chunk):
     # ceil(C / 64) a multiple of 8: workgroups map to (batch, channel tile)
     # through the XCD-contiguous order (across batch rows for B = 3), with ragged last tiles
@@ -291,7 +295,7 @@ def test_chain_order_across_xcds(B, T, C, algo, chunk):
 
 
 @pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("two_pass", 64), ("chunked", 128), ("two_pass", 128),
-                                        ("auto", 0), ("chunked", 512)])
+                                        ("auto", 0), ("chunked", 512), ("chunked", 16), ("two_pass", 32)])
 def test_deterministic(algo, chunk):
     """Two runs give bitwise equal outputs and states (the look-back folds its predecessors in a
     fixed order whatever the timing); auto takes the 128-token single pass that the fp16
@@ -336,7 +340,7 @@ def test_negative_controls_fail_the_gate():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[0] != "two_pass" or a[1] <= 64] + LONG)
+@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[0] != "two_pass" or a[1] <= 64] + LONG + SHORT)
 def test_workload_169m_fp32(algo, chunk):
     """B1 T1024 C768, fp32 k, v ~ N(0,1), empty state, y = wkv (fp32): bar 1e-5."""
     case = wi.workload_inputs(0)
@@ -346,7 +350,7 @@ def test_workload_169m_fp32(algo, chunk):
     check_state(st, ref, f"169m fp32 {algo}/{chunk}")
 
 
-@pytest.mark.parametrize("algo,chunk", ALGOS + LONG)
+@pytest.mark.parametrize("algo,chunk", ALGOS + LONG + SHORT)
 def test_workload_169m_batch_f16(algo, chunk):
     """B8 T1024 C768, fp16 k, v, r, random prior state, y = sigmoid(r) wkv (fp16): bar 2e-3."""
     case = wi.workload_inputs(1)

@@ -14,7 +14,7 @@ import wkv_inputs as wi
 from gpu_util import TOL, check_output, check_state, host, note, to_dev, torch
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("chunk", [16, 64, 128, 256])
 def test_forced_give_up_is_reported_and_cleared(chunk):
     import rwkv_wkv_linear_amd as rw
     t = torch()

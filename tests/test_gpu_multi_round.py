@@ -2,7 +2,8 @@
 look-back runs over several rounds of workgroups (a tile's predecessors may already have
 retired, and anchor tiles carry the chain forward).  Each mode at a size past one round, with
 ragged last tiles, against the fp64 oracle element by element:
-  * gated with a prior state, in fp16 and in bfloat16;
+  * gated with a prior state, in fp16 (tiles of 16, 32 and 128 tokens, long tiles of 256 and
+    1024) and in bfloat16;
   * ungated with fp32 output;
   * fp32 inputs on 64-token tiles;
   * the time mix with its xk/xv outputs.
@@ -68,6 +69,21 @@ def test_multi_round_long_tiles(chunk):
     y, so = forward(case, chunk)
     check_output(host(y), _cache[key], TOL["f16"], f"multi-round long tiles chunk={chunk}", out_dtype="f16")
     check_state(host(so), _cache[key], f"multi-round long tiles chunk={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_multi_round_short_tiles(chunk):
+    """Tiles of 16 tokens (two 8-token waves, anchors every 8 tiles) and 32 tokens (four waves)
+    past one resident round: chains of 313 and 157 tiles with a ragged last tile."""
+    case = wi.forward_case(2, 5000, 1024, seed=87, in_dtype="f16", gated=True, prior=True)
+    waves = chunk // 8
+    assert_past_one_round(2, 5000, 1024, chunk, 3 * chunk * 64 * 2 + 4 * waves * 64 * 4)
+    key = "short tiles"
+    if key not in _cache:
+        _cache[key] = oracle.forward(case)
+    y, so = forward(case, chunk)
+    check_output(host(y), _cache[key], TOL["f16"], f"multi-round short tiles chunk={chunk}", out_dtype="f16")
+    check_state(host(so), _cache[key], f"multi-round short tiles chunk={chunk}")
 
 
 def test_multi_round_bf16_gated_prior():
