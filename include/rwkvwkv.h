@@ -116,11 +116,12 @@ typedef struct rwkv4_opts {
                                 NULL = ungated (y = wkv).  Must be NULL for timemix. */
     int32_t chunk_len;       /* chunked scan: tokens per workgroup tile; 0 = auto (128
                                 for 2-byte inputs (fp16, bf16), 64 for fp32), else a power
-                                of two in [16, 1024].  Up to 128 (2-byte) / 64 (fp32) the
-                                tile's rows are staged in LDS at once; longer tiles (the
-                                single-launch scan only) run as sub-tiles of that length,
-                                read twice (aggregate, then output).  The two-pass scan
-                                takes up to 128 (2-byte) / 64 (fp32): ERR_ARG above. */
+                                of two in [16, 1024].  The single-launch scan stages a
+                                tile's rows in LDS while they fit in 160 KB (2-byte inputs:
+                                up to 512 tokens ungated, 256 gated or time mix; fp32:
+                                half of those) and runs longer tiles as sub-tiles read
+                                twice (aggregate, then output).  The two-pass scan takes
+                                up to 128 (2-byte) / 64 (fp32): ERR_ARG above. */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per (device,
                                 stream), allocated on first use;

@@ -424,6 +424,23 @@ __device__ __forceinline__ void tile_chain(int64_t rem, int64_t tt, int rot, int
 // pass, decoupled look-back) or from tile aggregates a previous launch wrote (two passes).
 constexpr int PREFIX_LOOKBACK = 0, PREFIX_AGGS = 1;
 
+// LDS one workgroup may hold on gfx950 (the CU's 160 KB).
+constexpr size_t kTileLdsMax = 160 * 1024;
+
+// Longest chunk the single-launch scan stages in LDS as one tile: NT tensors of rows plus the
+// wave summaries, waves of 32 tokens (2-byte inputs, up to 16 waves ungated and 8 otherwise)
+// or 16 (fp32, up to 16 waves).
+template <typename TIn, int MODE>
+constexpr int staged_tile_max() {
+    constexpr int NT = MODE == MODE_PLAIN ? 2 : 3;
+    constexpr int L = sizeof(TIn) == 2 ? 32 : 16;
+    constexpr int maxS = (L == 32 && MODE != MODE_PLAIN) ? 8 : 16;
+    int S = maxS;
+    while (S > 4 && (size_t)NT * S * L * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * 4 > kTileLdsMax)
+        S /= 2;
+    return S * L;
+}
+
 constexpr float kGuardSpread = 40.f;
 constexpr float kGuardBonus = -20.f;
 constexpr float kGuardBonusMax = 30.f;
@@ -1065,8 +1082,9 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     }
 }
 
-// Long tiles: chunk_len CL above the LDS-staged tile length SUBW = S * L (4 waves of L tokens:
-// 128 tokens for 2-byte inputs, 64 for fp32).  A workgroup owns CL tokens of a chain as
+// Long tiles: chunk_len CL above the longest tile staged in LDS at once (staged_tile_max), in
+// sub-tiles of SUBW = S * L tokens (4 waves of L tokens: 128 tokens for 2-byte inputs, 64 for
+// fp32).  A workgroup owns CL tokens of a chain as
 // NSUB = CL / SUBW consecutive sub-tiles that pass one after another through the same LDS rows.
 // Pass 1 folds every sub-tile's wave summaries into the chunk's aggregate, which the tile
 // publishes for the later tiles of its chain (the last tile of a chain, which nothing waits
@@ -1302,10 +1320,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
 
 // 32 tokens per wave in 4 waves (128-token tiles): half as many tiles per chain, so a
 // quarter of the look-back reads; three 52 KB workgroups share a CU, and with that
-// occupancy each wave may hold its 32 weights in registers.
+// occupancy each wave may hold its 32 weights in registers.  Up to 8 waves (256-token tiles).
 template <typename TIn, typename TOut, int MODE, int PREFIX>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
     wkv_tile32_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp, int G) {
+    tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
+}
+
+// 16 waves of 32 tokens (512-token tiles, ungated only: the k and v rows fill 128 KB of LDS).
+template <typename TIn, typename TOut, int MODE, int PREFIX>
+__global__ void __launch_bounds__(1024)
+    wkv_tile32w_kernel(ForwardArgs a, ChunkWorkspace ws, int S, int nCT, int nTT, int TW, int M, int rot, int lp, int G) {
+    static_assert(MODE == MODE_PLAIN, "16 waves of staged gate rows do not fit in LDS");
     tile_body<TIn, TOut, MODE, 32, PREFIX>(a, ws, S, nCT, nTT, TW, M, rot, lp, G);
 }
 
@@ -1438,8 +1464,10 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     // fp16 time-mix at 64 tokens: LDS is allocated in granules that make 32 KB fit only 4
     // workgroups per CU (160 KB), 28 KB five.
     const size_t lds = (size_t)NT * chunk_len * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
-    if (lds > 65536) return hipErrorInvalidConfiguration;
-    if (blocks > 0x7fffffff || S < 1 || 64 * S > 256) return hipErrorInvalidConfiguration;
+    if (lds > kTileLdsMax) return hipErrorInvalidConfiguration;
+    if (blocks > 0x7fffffff || S < 1 || 64 * S > 1024) return hipErrorInvalidConfiguration;
+    constexpr bool kWide = L == 32 && MODE == MODE_PLAIN;  // 16-wave tiles of 32-token waves
+    if (L == 32 && S > (kWide ? 16 : 8)) return hipErrorInvalidConfiguration;
     if (PREFIX == PREFIX_AGGS && nTT > 1) {
         // first pass: aggregates of the first nTT - 1 time tiles (k and v rows only)
         const int64_t agg_blocks = a.B * (int64_t)nCT * (nTT - 1);
@@ -1450,9 +1478,15 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const void *kern = L == 32  ? reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>)
-                       : L == 8 ? reinterpret_cast<const void *>(&wkv_tile8_kernel<TIn, TOut, MODE, PREFIX>)
-                                : reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
+    const void *kern;  // only the kernels for L are instantiated
+    if constexpr (L == 32)
+        kern = reinterpret_cast<const void *>(&wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>);
+    else if constexpr (L == 8)
+        kern = reinterpret_cast<const void *>(&wkv_tile8_kernel<TIn, TOut, MODE, PREFIX>);
+    else
+        kern = reinterpret_cast<const void *>(&wkv_tile_kernel<TIn, TOut, MODE, PREFIX>);
+    if constexpr (kWide)
+        if (S > 8) kern = reinterpret_cast<const void *>(&wkv_tile32w_kernel<TIn, TOut, MODE, PREFIX>);
     const int64_t slots = resident_slots(kern, 64 * S, lds);
     // States go into the publishing XCD's L2 first when every tile of a chain runs on one XCD:
     // workgroup i runs on XCD i mod 8, tile (tt, chain r) is workgroup tt * G + r with G
@@ -1476,6 +1510,13 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     const bool one_xcd = rot == 0 && G % 8 == 0;
     const int lp = PREFIX == PREFIX_LOOKBACK && (a.publish == RWKV_PUBLISH_L2_FIRST ||
                                                  (a.publish == RWKV_PUBLISH_AUTO && one_xcd));
+    if constexpr (kWide) {
+        if (S > 8) {
+            hipLaunchKernelGGL((wkv_tile32w_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds,
+                               s, a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
+            return hipGetLastError();
+        }
+    }
     if constexpr (L == 32)
         hipLaunchKernelGGL((wkv_tile32_kernel<TIn, TOut, MODE, PREFIX>), dim3((unsigned)grid), dim3(64 * S), lds, s,
                            a, ws, S, nCT, nTT, chunk_len, M, rot, lp, (int)G);
@@ -1500,8 +1541,11 @@ hipError_t launch_long(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     const int64_t grid = BCT * nTT;
     if (grid > 0x7fffffff || chunk_len % (S * L) != 0 || BCT > 0x7fffffff) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)NT * S * L * kTileChannels * sizeof(TIn) + (size_t)4 * S * kTileChannels * sizeof(float);
-    const void *kern = L == 32 ? reinterpret_cast<const void *>(&wkv_long32_kernel<TIn, TOut, MODE>)
-                               : reinterpret_cast<const void *>(&wkv_long16_kernel<TIn, TOut, MODE>);
+    const void *kern;  // only the kernel for L is instantiated
+    if constexpr (L == 32)
+        kern = reinterpret_cast<const void *>(&wkv_long32_kernel<TIn, TOut, MODE>);
+    else
+        kern = reinterpret_cast<const void *>(&wkv_long16_kernel<TIn, TOut, MODE>);
     const int64_t slots = resident_slots(kern, 64 * S, lds);
     const int rot = (slots > 0 && grid > slots) ? 1 : 0;
     if constexpr (L == 32)
@@ -1514,17 +1558,18 @@ hipError_t launch_long(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
 }
 
 // 16- and 32-token tiles: 2 or 4 waves of 8 tokens; 64-token tiles: 4 waves of 16 tokens;
-// 128-token tiles: 4 waves of 32 tokens; longer chunks (up to kMaxChunk) as long tiles of such
-// sub-tiles.
+// longer tiles: waves of 32 tokens (2-byte inputs) or 16 (fp32), 4 to 16 of them, as long as
+// the tile's rows fit in LDS (ungated: 512 tokens of 2-byte rows, 256 of fp32; gated and time
+// mix: 256 and 128); longer chunks (up to kMaxChunk) as long tiles of 4-wave sub-tiles.
+// Measured on one MI355X, a staged tile beats the long tile of the same length, which reads
+// k and v twice: B1 T65536 C2048 fp16 -> fp32 at 256 tokens 233 against 332 us, at 512 268
+// against 321 us; the 14B time mix at 256 tokens 19.5 against 24.9 us.
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
     if (chunk_len <= 32) return launch_tile<TIn, TOut, MODE, 8, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
-    if constexpr (sizeof(TIn) == 2) {
-        if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
-        if (chunk_len > 128) return launch_long<TIn, TOut, MODE, 32>(a, chunk_len, ws, s);
-    } else {
-        if (chunk_len > 64) return launch_long<TIn, TOut, MODE, 16>(a, chunk_len, ws, s);
-    }
+    constexpr int L = sizeof(TIn) == 2 ? 32 : 16;
+    if (chunk_len > staged_tile_max<TIn, MODE>()) return launch_long<TIn, TOut, MODE, L>(a, chunk_len, ws, s);
+    if (chunk_len >= 4 * L) return launch_tile<TIn, TOut, MODE, L, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
 }
 
@@ -1578,8 +1623,8 @@ hipError_t RWKV_TU_NAME(launch_chunked_2pass)(const ForwardArgs &a, int chunk_le
 }
 
 #if RWKV_TU_IN == 0
-// Longest tile whose rows are staged in LDS at once (the two-pass scan's granularity); the
-// single-launch scan takes longer chunks as long tiles.
+// Longest tile the two-pass scan stages (four waves); the single-launch scan stages longer
+// tiles while their rows fit in LDS (staged_tile_max) and runs longer chunks as long tiles.
 int tile_max_len(int in_2byte) { return in_2byte ? 128 : 64; }
 
 bool auto_sequential(int64_t B, int64_t T, int64_t C) {

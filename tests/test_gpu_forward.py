@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 import oracle
 import wkv_inputs as wi
 from gpu_util import (TOL, canary_ok, check_output, check_state, host, note, poisoned, to_dev,
-                      torch)
+                      tol_for, torch)
 
 _cache = {}
 
@@ -71,6 +71,19 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     tol = TOL[in_dt] if out_dt == "f32" or in_dt == "f16" else TOL["f16"]
     check_output(y, ref, tol, f"ragged {in_dt}->{out_dt} {algo}/{chunk}", out_dtype=out_dt)
     check_state(st, ref, f"ragged {in_dt} {algo}/{chunk}")
+
+
+@pytest.mark.parametrize("in_dt,out_dt,chunk", [("f16", "f32", 256), ("f16", "f32", 512), ("f16", "f16", 512),
+                                                ("bf16", "bf16", 512), ("f32", "f32", 128), ("f32", "f32", 256)])
+def test_ungated_staged_tiles(in_dt, out_dt, chunk):
+    """Ungated tiles of 8 or 16 waves staged in LDS at once (up to 144 KB: 512 tokens of 2-byte
+    rows, 256 of fp32), with a prior state, T = 1000 ragged against the tile and its waves and
+    C = 200 against 64 channels."""
+    case = wi.forward_case(2, 1000, 200, seed=47, in_dtype=in_dt, out_dtype=out_dt, prior=True)
+    ref = oracle_forward(("ungated staged", in_dt, out_dt), case)
+    y, st = run(case, "chunked", chunk, label="ungated staged")
+    check_output(y, ref, tol_for(in_dt, out_dt), f"ungated staged {in_dt}->{out_dt} chunk={chunk}", out_dtype=out_dt)
+    check_state(st, ref, f"ungated staged {in_dt} chunk={chunk}")
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])

@@ -2,8 +2,8 @@
 look-back runs over several rounds of workgroups (a tile's predecessors may already have
 retired, and anchor tiles carry the chain forward).  Each mode at a size past one round, with
 ragged last tiles, against the fp64 oracle element by element:
-  * gated with a prior state, in fp16 (tiles of 16, 32 and 128 tokens, long tiles of 256 and
-    1024) and in bfloat16;
+  * gated with a prior state, in fp16 (tiles of 16, 32, 128 and 256 tokens, long tiles of 1024)
+    and in bfloat16;
   * ungated with fp32 output;
   * fp32 inputs on 64-token tiles;
   * the time mix with its xk/xv outputs.
@@ -59,8 +59,9 @@ def test_multi_round_gated_prior():
 
 @pytest.mark.parametrize("chunk", [256, 1024])
 def test_multi_round_long_tiles(chunk):
-    """Long tiles (chunks of 256 or 1024 tokens, 128-token sub-tiles) past one resident round, with
-    anchors (chains of 79 and 20 tiles) and a ragged last tile."""
+    """Chunks of 256 tokens (8-wave tiles staged in LDS) and 1024 tokens (long tiles of 128-token
+    sub-tiles) past one resident round, with anchors (chains of 79 and 20 tiles) and a ragged
+    last tile."""
     case = wi.forward_case(2, 20000, 2048, seed=86, in_dtype="f16", gated=True, prior=True)
     assert_past_one_round(2, 20000, 2048, chunk, 3 * 128 * 64 * 2)
     key = "long tiles"
