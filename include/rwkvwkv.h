@@ -120,8 +120,8 @@ typedef struct rwkv4_opts {
                                 tile's rows in LDS while they fit in 160 KB (2-byte inputs:
                                 up to 512 tokens ungated, 256 gated or time mix; fp32:
                                 half of those) and runs longer tiles as sub-tiles read
-                                twice (aggregate, then output).  The two-pass scan takes
-                                up to 128 (2-byte) / 64 (fp32): ERR_ARG above. */
+                                twice (aggregate, then output).  The two-pass scan stages
+                                whole tiles only: RWKV_ERR_ARG above that limit. */
     int32_t algo;            /* rwkv_algo */
     void *workspace;         /* chunked scan scratch: NULL = library-cached per (device,
                                 stream), allocated on first use;
@@ -213,7 +213,8 @@ rwkv_status rwkv4_timemix_fused(int64_t B, int64_t T, int64_t C,
  * B * ceil(C / 64) * ceil(T / chunk_len) = 16384 tiles (B1 T65536 C2048 with 128-token
  * chunks; B1 T1024 C5120 needs 640), else RWKV_ERR_ARG.
  *   opts->workspace must be NULL and opts->algo must not be RWKV_ALGO_CHUNKED (RWKV_ERR_ARG);
- *   chunk_len is the two-pass scan's (at most 128 for 2-byte inputs, 64 for fp32).
+ *   chunk_len is the two-pass scan's (at most 256 tokens for 2-byte inputs, 128 for fp32: the
+ *   time mix stages three tensors of rows).
  * Every call on a GPU shares that GPU's scratch, and nothing in it needs clearing (each call
  * writes the aggregates it reads): calls that may run at the same time on one GPU (different
  * streams, or graphs replayed concurrently) race on it and must be serialised by the caller.

@@ -243,13 +243,13 @@ rwkv_status run_forward(ForwardArgs &a, const Resolved &o, hipStream_t stream) {
         return ok();
     }
     const int chunk = o.chunk_len ? o.chunk_len : auto_chunk_len(B, T, C, ei == 2);
-    const int tmax = tile_max_len(ei == 2);
+    const int tmax = tile_max_len(ei == 2, a.mode != MODE_PLAIN);
     const int64_t nTT = (T + chunk - 1) / chunk;
     bool two_pass = o.algo == RWKV_ALGO_TWO_PASS || o.static_scratch ||
                     (o.algo == RWKV_ALGO_AUTO && nTT <= kTwoPassMaxTiles);
     if (two_pass && chunk > tmax)
-        return fail(RWKV_ERR_ARG, "the two-pass scan takes chunk_len up to %d for this input dtype (got %d); longer "
-                                  "chunks run in the single-launch scan", tmax, chunk);
+        return fail(RWKV_ERR_ARG, "the two-pass scan takes chunk_len up to %d for this input dtype and mode (got %d); "
+                                  "longer chunks run in the single-launch scan", tmax, chunk);
     const int64_t tiles = B * ((C + kTileChannels - 1) / kTileChannels) * nTT;
     if (T > chunk && o.static_scratch && (size_t)tiles * kTileChannels * 16 > kStaticScratchBytes)
         return fail(RWKV_ERR_ARG, "%lld tiles need %zu bytes of scratch, more than the %zu this entry point holds "

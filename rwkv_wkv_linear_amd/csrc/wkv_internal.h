@@ -62,11 +62,11 @@ struct ChunkWorkspace {
 constexpr int kTileChannels = 64;  // channels per workgroup tile
 constexpr int kMinChunk = 16, kMaxChunk = 1024;
 
-// Longest tile of the two-pass scan: 128 tokens for 2-byte inputs, 64 for fp32.  The
-// single-launch scan stages tiles of up to 160 KB of rows in LDS (2-byte inputs: 512 tokens
-// ungated, 256 gated or time mix; fp32: half of those) and runs longer chunks (up to kMaxChunk)
-// as long tiles of 4-wave sub-tiles.
-int tile_max_len(int in_2byte);
+// Longest tile staged in LDS at once (160 KB of rows and wave summaries): for 2-byte inputs 512
+// tokens ungated and 256 gated or time mix (a third tensor of rows), for fp32 half of those.
+// The two-pass scan takes chunk lengths up to it; the single-launch scan runs longer chunks
+// (up to kMaxChunk) as long tiles of 4-wave sub-tiles.
+int tile_max_len(int in_2byte, int gated);
 // Chunk length (tokens per workgroup tile) the auto policy picks for a shape.
 int auto_chunk_len(int64_t B, int64_t T, int64_t C, int in_2byte);
 // True when the auto policy picks the sequential kernel.

@@ -1573,11 +1573,14 @@ hipError_t launch_chunk_t(const ForwardArgs &a, int chunk_len, const ChunkWorksp
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_LOOKBACK>(a, chunk_len, ws, s);
 }
 
+// The two-pass scan stages every tile whole (chunk_len up to staged_tile_max, checked by the
+// caller), in the same tile shapes as the single pass.
 template <typename TIn, typename TOut, int MODE>
 hipError_t launch_chunk2_t(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws, hipStream_t s) {
     if (chunk_len <= 32) return launch_tile<TIn, TOut, MODE, 8, PREFIX_AGGS>(a, chunk_len, ws, s);
-    if constexpr (sizeof(TIn) == 2)
-        if (chunk_len == 128) return launch_tile<TIn, TOut, MODE, 32, PREFIX_AGGS>(a, chunk_len, ws, s);
+    constexpr int L = sizeof(TIn) == 2 ? 32 : 16;
+    if (chunk_len > staged_tile_max<TIn, MODE>()) return hipErrorInvalidValue;
+    if (chunk_len >= 4 * L) return launch_tile<TIn, TOut, MODE, L, PREFIX_AGGS>(a, chunk_len, ws, s);
     return launch_tile<TIn, TOut, MODE, 16, PREFIX_AGGS>(a, chunk_len, ws, s);
 }
 
@@ -1623,9 +1626,13 @@ hipError_t RWKV_TU_NAME(launch_chunked_2pass)(const ForwardArgs &a, int chunk_le
 }
 
 #if RWKV_TU_IN == 0
-// Longest tile the two-pass scan stages (four waves); the single-launch scan stages longer
-// tiles while their rows fit in LDS (staged_tile_max) and runs longer chunks as long tiles.
-int tile_max_len(int in_2byte) { return in_2byte ? 128 : 64; }
+// Longest tile staged in LDS at once (the two-pass scan's limit; the single-launch scan runs
+// longer chunks as long tiles).
+int tile_max_len(int in_2byte, int gated) {
+    if (in_2byte)
+        return gated ? staged_tile_max<_Float16, MODE_GATED>() : staged_tile_max<_Float16, MODE_PLAIN>();
+    return gated ? staged_tile_max<float, MODE_GATED>() : staged_tile_max<float, MODE_PLAIN>();
+}
 
 bool auto_sequential(int64_t B, int64_t T, int64_t C) {
     // Enough independent (b, channel) lanes to fill every SIMD twice over: the

@@ -97,13 +97,18 @@ def test_opts_without_publish_field_accepted():
 
 
 def test_two_pass_chunk_len_limit():
-    # the two-pass scan stages a whole tile in LDS: 128 tokens at most for 2-byte inputs, 64 for
-    # fp32; longer chunks (up to 1024) run only in the single-launch scan, as long tiles
-    for c in (256, 512, 1024):
+    # the two-pass scan stages whole tiles in LDS (160 KB): gated 2-byte rows up to 256 tokens,
+    # ungated up to 512, fp32 half of those; longer chunks (up to 1024) run only in the
+    # single-launch scan, as long tiles
+    for c in (512, 1024):
         o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, r=P + 0x400000, chunk_len=c,
                  algo=rw.RWKV_ALGO_TWO_PASS)
         assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "two-pass" in rw.rwkv_last_error()
-    o = opts(chunk_len=128, algo=rw.RWKV_ALGO_TWO_PASS)
+    o = opts(in_dtype=rw.RWKV_F16, out_dtype=rw.RWKV_F16, chunk_len=1024, algo=rw.RWKV_ALGO_TWO_PASS)
+    assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "two-pass" in rw.rwkv_last_error()
+    o = opts(chunk_len=512, algo=rw.RWKV_ALGO_TWO_PASS)
+    assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "two-pass" in rw.rwkv_last_error()
+    o = opts(r=P + 0x400000, chunk_len=256, algo=rw.RWKV_ALGO_TWO_PASS)
     assert fwd(T=4096, o=o) == rw.RWKV_ERR_ARG and "two-pass" in rw.rwkv_last_error()
 
 

@@ -42,8 +42,6 @@ ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 128)
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "bf16"), ("f32", "bf16")])
 @pytest.mark.parametrize("algo,chunk", ALGOS)
 def test_forward_ragged_gated_prior(in_dt, out_dt, algo, chunk):
-    if in_dt == "f32" and algo == "two_pass" and chunk > 64:
-        pytest.skip("fp32 inputs: the two-pass scan takes tiles of at most 64 tokens (LDS budget)")
     case = wi.forward_case(2, 1000, 200, seed=141, in_dtype=in_dt, out_dtype=out_dt, gated=True, prior=True)
     key = ("ragged", in_dt)
     if key not in _cache:

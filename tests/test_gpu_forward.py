@@ -46,15 +46,11 @@ def run(case, algo="auto", chunk_len=0, state_out=True, y_dtype=None, label=""):
 
 
 ALGOS = [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64), ("two_pass", 128), ("auto", 0)]
-# chunks longer than the LDS-staged tile (128 tokens for 2-byte inputs, 64 for fp32): long tiles
+# chunks longer than four waves: tiles of 8 or 16 waves while their rows fit in LDS, else long
+# tiles (gated 2-byte rows: 512 and 1024; fp32: 256 and above)
 LONG = [("chunked", 256), ("chunked", 512), ("chunked", 1024)]
 # chunks shorter than 64 tokens: waves of 8 tokens (4 of them, or 2 with anchors every 8 tiles)
 SHORT = [("chunked", 16), ("chunked", 32), ("two_pass", 16), ("two_pass", 32)]
-
-
-def skip_unsupported(in_dt, algo, chunk):
-    if in_dt == "f32" and algo == "two_pass" and chunk > 64:
-        pytest.skip("fp32 inputs: the two-pass scan takes tiles of at most 64 tokens (LDS budget)")
 
 
 # ----------------------------------------------------------------------------- small, ragged
@@ -64,7 +60,6 @@ def skip_unsupported(in_dt, algo, chunk):
 def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     # T = 1000 is ragged against 16-token sub-chunks and every tile length; C = 200 against 64.
     # With chunks of 256 or 512 the last tile is partial (a partial sub-tile); 1024 is one tile.
-    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(2, 1000, 200, seed=41, in_dtype=in_dt, out_dtype=out_dt, gated=True, prior=True)
     ref = oracle_forward(("ragged", in_dt), case)
     y, st = run(case, algo, chunk, label="ragged")
@@ -73,17 +68,18 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     check_state(st, ref, f"ragged {in_dt} {algo}/{chunk}")
 
 
+@pytest.mark.parametrize("algo", ["chunked", "two_pass"])
 @pytest.mark.parametrize("in_dt,out_dt,chunk", [("f16", "f32", 256), ("f16", "f32", 512), ("f16", "f16", 512),
                                                 ("bf16", "bf16", 512), ("f32", "f32", 128), ("f32", "f32", 256)])
-def test_ungated_staged_tiles(in_dt, out_dt, chunk):
+def test_ungated_staged_tiles(in_dt, out_dt, chunk, algo):
     """Ungated tiles of 8 or 16 waves staged in LDS at once (up to 144 KB: 512 tokens of 2-byte
     rows, 256 of fp32), with a prior state, T = 1000 ragged against the tile and its waves and
     C = 200 against 64 channels."""
     case = wi.forward_case(2, 1000, 200, seed=47, in_dtype=in_dt, out_dtype=out_dt, prior=True)
     ref = oracle_forward(("ungated staged", in_dt, out_dt), case)
-    y, st = run(case, "chunked", chunk, label="ungated staged")
-    check_output(y, ref, tol_for(in_dt, out_dt), f"ungated staged {in_dt}->{out_dt} chunk={chunk}", out_dtype=out_dt)
-    check_state(st, ref, f"ungated staged {in_dt} chunk={chunk}")
+    y, st = run(case, algo, chunk, label="ungated staged")
+    check_output(y, ref, tol_for(in_dt, out_dt), f"ungated staged {in_dt}->{out_dt} {algo}/{chunk}", out_dtype=out_dt)
+    check_state(st, ref, f"ungated staged {in_dt} {algo}/{chunk}")
 
 
 @pytest.mark.parametrize("C", [203, 13, 1, 64, 67])
@@ -242,7 +238,6 @@ def test_bonus_outside_the_linear_space_guard(in_dt, algo, chunk):
     """Channels with u = -25 (below the fast path's bonus guard: the current token's weight would
     underflow against the others) and u = +40 (above it: e^u times a weight of up to e^40
     overflows fp32) take the exact per-token recurrence; their neighbours stay on the fast path."""
-    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(2, 1000, 192, seed=54, in_dtype=in_dt, out_dtype="f32", gated=True, prior=True)
     u = case["u"].copy()
     u[0::5] = -25.0
@@ -261,7 +256,6 @@ def test_incoming_state_outside_the_linear_space_guard(in_dt, algo, chunk):
     keeps a log-scale near 70 - 0.0067 n for thousands of tokens, so the waves of later tiles
     start more than 60 nats above their own largest key (the incoming-state guard) and take the
     exact recurrence, until the scale has decayed back inside the guard (after ~1000 tokens)."""
-    skip_unsupported(in_dt, algo, chunk)
     case = wi.forward_case(1, 2048, 128, seed=55, in_dtype=in_dt, out_dtype="f32", prior=False)
     k = case["k"].astype(np.float64)
     k[0, 5, 0:8] = 70.0
@@ -308,7 +302,8 @@ def test_chain_order_across_xcds(B, T, C, algo, chunk):
 
 
 @pytest.mark.parametrize("algo,chunk", [("chunked", 64), ("two_pass", 64), ("chunked", 128), ("two_pass", 128),
-                                        ("auto", 0), ("chunked", 512), ("chunked", 16), ("two_pass", 32)])
+                                        ("auto", 0), ("chunked", 512), ("chunked", 16), ("two_pass", 32),
+                                        ("two_pass", 256)])
 def test_deterministic(algo, chunk):
     """Two runs give bitwise equal outputs and states (the look-back folds its predecessors in a
     fixed order whatever the timing); auto takes the 128-token single pass that the fp16
@@ -353,7 +348,7 @@ def test_negative_controls_fail_the_gate():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("algo,chunk", [a for a in ALGOS if a[0] != "two_pass" or a[1] <= 64] + LONG + SHORT)
+@pytest.mark.parametrize("algo,chunk", ALGOS + LONG + SHORT + [("two_pass", 256)])
 def test_workload_169m_fp32(algo, chunk):
     """B1 T1024 C768, fp32 k, v ~ N(0,1), empty state, y = wkv (fp32): bar 1e-5."""
     case = wi.workload_inputs(0)

@@ -153,9 +153,10 @@ def test_auto_forward_under_capture_takes_two_pass():
 
 
 def test_capture_refuses_what_cannot_replay():
-    """On a capturing stream the single-launch chunked scan (explicit, or a chunk_len above 128,
-    which only it runs) and the library-cached workspace are refused before anything is enqueued; a call whose T fits in one tile needs neither and is
-    captured as it is."""
+    """On a capturing stream the single-launch chunked scan (explicit, or a chunk_len above the
+    longest tile staged in LDS, 256 tokens for gated 2-byte rows, which only it runs) and the
+    library-cached workspace are refused before anything is enqueued; a call whose T fits in one
+    tile needs neither and is captured as it is."""
     import rwkv_wkv_linear_amd as rw
     t = torch()
     B1, T1, C1 = 1, 600, 128
@@ -174,7 +175,7 @@ def test_capture_refuses_what_cannot_replay():
     with t.cuda.stream(side):
         with t.cuda.graph(graph):
             for kw in (dict(algo="chunked", workspace=ws), dict(algo="auto"), dict(algo="two_pass"),
-                       dict(algo="auto", chunk_len=256, workspace=ws)):
+                       dict(algo="auto", chunk_len=512, workspace=ws)):
                 try:
                     rw.rwkv4_wkv_forward(d["k"], d["v"], d["w"], d["u"], y=y, state_in=d["state_in"], r=d["r"], **kw)
                 except rw.RwkvError as e:

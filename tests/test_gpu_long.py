@@ -2,8 +2,9 @@
 fp16 k ~ N(0, 2), v ~ N(0, 1), fp32 output and final state, chunk length swept over
 64, 128, 256, 512 and 1024 tokens and the automatic choice (128), checked element by
 element against the fp64 oracle's recurrence, which is itself checked against the
-direct sums at sampled points.  Chunks above 128 tokens run as long tiles (128-token
-sub-tiles read twice), and every chain has more than 16 tiles, so anchors are used."""
+direct sums at sampled points.  Chunks of 256 and 512 tokens run as tiles of 8 and 16 waves
+staged in LDS at once, 1024 as long tiles (128-token sub-tiles read twice), and every chain
+has more than 16 tiles, so anchors are used."""
 import numpy as np
 import pytest
 

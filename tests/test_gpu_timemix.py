@@ -62,7 +62,7 @@ def check_all(out, ref, case, what, with_xkv):
 
 @pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64),
                                         ("two_pass", 128), ("chunked", 256), ("chunked", 512), ("chunked", 1024),
-                                        ("chunked", 16), ("two_pass", 32)])
+                                        ("chunked", 16), ("two_pass", 32), ("two_pass", 256)])
 @pytest.mark.parametrize("with_xkv", [False, True])
 def test_ragged_prior(algo, chunk, with_xkv):
     case = wi.timemix_case(2, 777, 136, seed=61, prior=True)
@@ -100,7 +100,8 @@ def test_zero_tokens():
 
 
 @pytest.mark.parametrize("algo,chunk", [("auto", 0), ("sequential", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 64),
-                                        ("two_pass", 128), ("chunked", 256), ("chunked", 1024), ("chunked", 32)])
+                                        ("two_pass", 128), ("chunked", 256), ("chunked", 1024), ("chunked", 32),
+                                        ("two_pass", 256)])
 def test_workload_14b_layer(algo, chunk):
     """B1 T1024 C5120 fp16, token shift from x_prev, r = xr, y = sigmoid(xr) wkv (fp16)."""
     case = wi.workload_inputs(2)
