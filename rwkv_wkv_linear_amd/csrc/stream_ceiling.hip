@@ -5,7 +5,10 @@
 // the cost of its arithmetic and of its dependencies.
 //
 //   wkvceil_tile    the chunked scan's pattern: one workgroup of 4 waves per (batch row, 64-channel
-//                   tile, time tile of 4 x L tokens), blockIdx time-tile-major; each wave copies
+//                   tile, time tile of 4 x L tokens), blockIdx time-tile-major, the (batch row,
+//                   channel tile) of an index chosen as the scan chooses it (with 8 XCDs and a
+//                   multiple of 8 channel tiles, each XCD takes a contiguous range, rotated from
+//                   one time tile to the next when the grid exceeds one resident round); each wave copies
 //                   its L rows of every input into LDS with 16-byte global-to-LDS loads carrying
 //                   the non-temporal hint, waits, and writes its L rows of the output from LDS
 //                   with 16-byte non-temporal stores.  The LDS size is the scan kernel's, so the
@@ -35,13 +38,16 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 // esz_in / esz_out: element bytes (2 or 4); n_in inputs (up to 3), one output.
 __global__ void __launch_bounds__(256) tile_kernel(const char *in0, const char *in1, const char *in2, int n_in,
                                                    char *out, int64_t B, int64_t T, int64_t C, int L, int esz_in,
-                                                   int esz_out, int lds_rows) {
+                                                   int esz_out, int lds_rows, int rot) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nCT = (int)((C + kTileChannels - 1) / kTileChannels);
     const int64_t BCT = B * nCT;
     const int TW = 4 * L;
-    const int64_t tt = blockIdx.x / BCT, r = blockIdx.x - tt * BCT;
+    const int64_t tt = blockIdx.x / BCT, rem = blockIdx.x - tt * BCT;
+    // workgroup i runs on XCD i mod 8: index rem takes chain (rem % 8) * (BCT / 8) + rem / 8 when
+    // nCT is a multiple of 8, so that each XCD reads a contiguous range of channel tiles
+    const int64_t r = (nCT % 8 == 0) ? ((rem + (rot ? tt : 0)) % 8) * (BCT / 8) + rem / 8 : rem;
     const int64_t b = r / nCT, ct = r - b * nCT;
     const int64_t t0 = tt * TW + (int64_t)wv * L;
     const char *src[3] = {in0, in1, in2};
@@ -132,8 +138,15 @@ int wkvceil_tile(const void *in0, const void *in1, const void *in2, int n_in, vo
         (esz_out != 2 && esz_out != 4) || lds_bytes < n_in * 4 * L * 64 * esz_in)
         return -1;
     const int64_t grid = B * (C / 64) * ((T + 4 * L - 1) / (4 * L));
+    int per_cu = 0, cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tile_kernel, 256, lds_bytes) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -4;
+    const int rot = grid > (int64_t)per_cu * cus ? 1 : 0;  // more than one resident round
     hipLaunchKernelGGL(tile_kernel, dim3((unsigned)grid), dim3(256), lds_bytes, s, (const char *)in0,
-                       (const char *)in1, (const char *)in2, n_in, (char *)out, B, T, C, L, esz_in, esz_out, 4 * L);
+                       (const char *)in1, (const char *)in2, n_in, (char *)out, B, T, C, L, esz_in, esz_out, 4 * L,
+                       rot);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
