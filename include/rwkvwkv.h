@@ -150,9 +150,10 @@ typedef struct rwkv4_opts {
  * that passes one workspace to several streams must serialise them itself.
  * Graph capture.  The single-launch chunked scan stamps its workspace per launch from the
  * host, so it cannot be replayed from a graph: on a capturing stream AUTO takes the two-pass
- * scan, which needs opts->workspace (RWKV_ERR_ARG without it), and RWKV_ALGO_CHUNKED is
- * refused with RWKV_ERR_ARG.  The sequential algorithm, and any call whose T fits in one tile,
- * capture as they are.
+ * scan, which needs opts->workspace (RWKV_ERR_ARG without it), and RWKV_ALGO_CHUNKED, or a
+ * chunk_len longer than the longest tile staged in LDS (which only the single-launch scan runs),
+ * is refused with RWKV_ERR_ARG.  The sequential algorithm, and any call whose T fits in one
+ * tile, capture as they are.
  * In the single-launch chunked scan a tile waits for the published states of earlier tiles
  * of its chain, which were dispatched before it, so the wait ends even when other kernels
  * share the GPU.  Each wait is still bounded (tens of milliseconds of polling): a wait that
