@@ -68,15 +68,17 @@ def test_ragged_gated_prior(in_dt, out_dt, algo, chunk):
     check_state(st, ref, f"ragged {in_dt} {algo}/{chunk}")
 
 
+@pytest.mark.parametrize("C", [200, 203])
 @pytest.mark.parametrize("algo", ["chunked", "two_pass"])
 @pytest.mark.parametrize("in_dt,out_dt,chunk", [("f16", "f32", 256), ("f16", "f32", 512), ("f16", "f16", 512),
                                                 ("bf16", "bf16", 512), ("f32", "f32", 128), ("f32", "f32", 256)])
-def test_ungated_staged_tiles(in_dt, out_dt, chunk, algo):
+def test_ungated_staged_tiles(in_dt, out_dt, chunk, algo, C):
     """Ungated tiles of 8 or 16 waves staged in LDS at once (up to 144 KB: 512 tokens of 2-byte
     rows, 256 of fp32), with a prior state, T = 1000 ragged against the tile and its waves and
-    C = 200 against 64 channels."""
-    case = wi.forward_case(2, 1000, 200, seed=47, in_dtype=in_dt, out_dtype=out_dt, prior=True)
-    ref = oracle_forward(("ungated staged", in_dt, out_dt), case)
+    C ragged against 64 channels; C = 203 is no whole number of 16-byte chunks either, so each
+    lane stages its own channel."""
+    case = wi.forward_case(2, 1000, C, seed=47, in_dtype=in_dt, out_dtype=out_dt, prior=True)
+    ref = oracle_forward(("ungated staged", in_dt, out_dt, C), case)
     y, st = run(case, algo, chunk, label="ungated staged")
     check_output(y, ref, tol_for(in_dt, out_dt), f"ungated staged {in_dt}->{out_dt} {algo}/{chunk}", out_dtype=out_dt)
     check_state(st, ref, f"ungated staged {in_dt} {algo}/{chunk}")
@@ -94,7 +96,8 @@ def test_odd_channels(C, algo, chunk):
     check_state(st, ref, f"C={C} {algo}/{chunk}")
 
 
-@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("two_pass", 64)])
+@pytest.mark.parametrize("algo,chunk", [("sequential", 0), ("chunked", 64), ("two_pass", 64), ("chunked", 16),
+                                        ("chunked", 128), ("two_pass", 256)])
 def test_misaligned_pointers(algo, chunk):
     """Tensors offset by one element: the library must take the per-element path."""
     import rwkv_wkv_linear_amd as rw
