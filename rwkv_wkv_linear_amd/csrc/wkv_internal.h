@@ -94,9 +94,9 @@ hipError_t launch_chunked(const ForwardArgs &a, int chunk_len, const ChunkWorksp
 hipError_t launch_chunked_2pass(const ForwardArgs &a, int chunk_len, const ChunkWorkspace &ws,
                                 hipStream_t s);
 // Longest chain (time tiles per (b, channel tile)) the two-pass scan takes by default: none.
-// Measured on the 14B layer shape, the aggregate pass (8.1 us) plus the emit pass (13.8 us)
-// cost more than the single pass's look-back wait (18.7 us in all), so AUTO keeps the single
-// pass; RWKV_ALGO_TWO_PASS stays available (graph-capturable, no cross-workgroup waiting).
+// Measured on the 14B layer shape, the two launches take 19.8 us against 12.7 us for the
+// single pass with its look-back, so AUTO keeps the single pass; RWKV_ALGO_TWO_PASS stays
+// available (graph-capturable, no cross-workgroup waiting).
 constexpr int kTwoPassMaxTiles = 0;
 // T == 0: state_out <- state_in (or the empty state), x_last <- x_prev (or zeros).
 hipError_t launch_passthrough(const ForwardArgs &a, hipStream_t s);

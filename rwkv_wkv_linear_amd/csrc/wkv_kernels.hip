@@ -1467,7 +1467,9 @@ hipError_t launch_tile(const ForwardArgs &a, int chunk_len, const ChunkWorkspace
     if (lds > kTileLdsMax) return hipErrorInvalidConfiguration;
     if (blocks > 0x7fffffff || S < 1 || 64 * S > 1024) return hipErrorInvalidConfiguration;
     constexpr bool kWide = L == 32 && MODE == MODE_PLAIN;  // 16-wave tiles of 32-token waves
-    if (L == 32 && S > (kWide ? 16 : 8)) return hipErrorInvalidConfiguration;
+    // each kernel's launch bounds: 8-token waves up to 4 per workgroup, 32-token waves up to 8
+    // (16 ungated), 16-token waves up to 16
+    if ((L == 8 && S > 4) || (L == 32 && S > (kWide ? 16 : 8))) return hipErrorInvalidConfiguration;
     if (PREFIX == PREFIX_AGGS && nTT > 1) {
         // first pass: aggregates of the first nTT - 1 time tiles (k and v rows only)
         const int64_t agg_blocks = a.B * (int64_t)nCT * (nTT - 1);
