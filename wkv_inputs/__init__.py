@@ -146,6 +146,23 @@ def forward_case(B, T, C, *, seed, in_dtype="f32", out_dtype=None, gated=False,
                 in_dtype=in_dtype, out_dtype=out_dtype or in_dtype)
 
 
+def device_forward_case(B, T, C, *, seed, k_sigma=1.0, device="cuda:0"):
+    """Inputs for rwkv4_wkv_forward too large to draw on the host: fp16 k ~ N(0, k_sigma^2) and
+    v ~ N(0, 1) drawn on the device by torch's generator seeded with `seed` (fp32 draws rounded
+    once to fp16, RNE), w and u by the recipe above.  Whoever checks results copies back the
+    rows or columns it needs; both sides read the identical fp16 values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    k = torch.randn((B, T, C), generator=g, device=device, dtype=torch.float32)
+    if k_sigma != 1.0:
+        k.mul_(k_sigma)
+    k = k.to(torch.float16)
+    v = torch.randn((B, T, C), generator=g, device=device, dtype=torch.float32).to(torch.float16)
+    w, u = decay_bonus(C)
+    return dict(B=B, T=T, C=C, w=w, u=u, k=k, v=v)
+
+
 def timemix_case(B, T, C, *, seed, in_dtype="f16", out_dtype=None, index=2, prior=False):
     """Inputs for rwkv4_timemix_fused.
     Draw order: x, x_prev, mix_k, mix_v, mix_r, k, v, [aa, bb, pp]."""
