@@ -123,7 +123,8 @@ def counters_traffic():
 
 def cpu_baseline(name, case, elements, sample):
     """The fp64 oracle as it stands, on the host cores: median of repeated runs over `case`
-    (at least 3, about CPU_BUDGET_S seconds in all), then one run on a single thread.  Every
+    (at least 3, about CPU_BUDGET_S seconds in all), then one run on a single thread.  Returns
+    the line's object and the oracle's result of the last run.  Every
     oracle routine is C with OpenMP over independent lanes (channels, or rows and elements for
     the mixers); numpy only marshals the arrays and, for the prologue, runs the token shift's
     elementwise mix."""
@@ -135,9 +136,10 @@ def cpu_baseline(name, case, elements, sample):
     threads = oracle.num_threads()
     times = []
     t_end = time.perf_counter() + CPU_BUDGET_S
+    ref = None
     while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
         t0 = time.perf_counter()
-        run(case)
+        ref = run(case)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     out = {
@@ -165,7 +167,25 @@ def cpu_baseline(name, case, elements, sample):
         out["value_one_thread"] = elements / (time.perf_counter() - t0)
         if prev is not None:
             oracle.set_threads(prev)
-    return out
+    return out, ref
+
+
+# Bars of the parity tests for the WKV output (scaled error, by input dtype) and the final state
+PARITY_TOL = {"f32": 1e-5, "f16": 2e-3}
+STATE_TOL = 1e-5
+
+
+def parity(su, ref):
+    """Error of the timed launches' outputs (those of the first buffer set; every set holds the
+    same inputs) against the oracle's result on those inputs, by the parity tests' metrics."""
+    from oracle import compare as cmp
+    host = lambda t: t.float().cpu().numpy().astype("float64")  # noqa: E731
+    y = host(su.check_out["y"])
+    err = cmp.scaled_error(y, ref["y"], ref["scale"], cmp.FLOOR[su.out_dtype])
+    ea, eb = cmp.state_error(host(su.check_out["state"]), ref["state"], ref["state_abs"])
+    tol = PARITY_TOL[su.in_dtype]
+    return {"vs": "oracle", "scaled_error": err, "tol": tol, "state_error": max(ea, eb), "state_tol": STATE_TOL,
+            "within_tol": bool(err <= tol and max(ea, eb) <= STATE_TOL)}
 
 def copy_kernel(args):
     import torch
@@ -285,6 +305,10 @@ class Setup:
         ei, eo = esz[wl.in_dtype], esz[wl.out_dtype]
         name16 = "bf16" if args.bf16 else "f16"
         self.io = f"{wl.in_dtype}->{wl.out_dtype}".replace("f16", name16)
+        self.in_dtype, self.out_dtype = wl.in_dtype, wl.out_dtype
+        # outputs of the first buffer set, checked against the oracle (WKV workloads whose device
+        # inputs are the oracle's: not under --bf16, which rounds them again)
+        self.check_out = None
 
         def dev_t(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -356,6 +380,8 @@ class Setup:
                     s["xk"] = torch.empty((B, T, C), dtype=tdt[wl.in_dtype], device=dev)
                     s["xv"] = torch.empty((B, T, C), dtype=tdt[wl.in_dtype], device=dev)
                 self.keep.append(s)
+                if self.check_out is None and not args.bf16:
+                    self.check_out = {"y": s["y"], "state": s["state_out"]}
                 self.sets.append([(B, T, C, vp(s["x"].data_ptr()), vp(sh["x_prev"].data_ptr()),
                                    vp(s["x_last"].data_ptr()), vp(sh["mix_k"].data_ptr()),
                                    vp(sh["mix_v"].data_ptr()), vp(sh["mix_r"].data_ptr()),
@@ -390,6 +416,8 @@ class Setup:
                 o.r = s["r"].data_ptr() if wl.gated else None
                 s["opts"] = o
                 self.keep.append(s)
+                if self.check_out is None and not args.bf16:
+                    self.check_out = {"y": s["y"], "state": s["state_out"]}
                 self.sets.append([(B, T, C, vp(sh["w"].data_ptr()), vp(sh["u"].data_ptr()),
                                    vp(s["k"].data_ptr()), vp(s["v"].data_ptr()), vp(s["y"].data_ptr()),
                                    vp(sh["state_in"].data_ptr()) if wl.prior else None,
@@ -568,8 +596,10 @@ def main():
         if result["ceiling"]:
             result["ceiling"]["kernel_over_ceiling"] = (launch_avg_ms * 1e3
                                                         / result["ceiling"]["same_pattern"]["kernel_avg_us"])
-    result["cpu_baseline"] = None if args.no_cpu_baseline else \
+    result["cpu_baseline"], ref = (None, None) if args.no_cpu_baseline else \
         cpu_baseline(name, su.cpu_case, su.cpu_elements, su.cpu_sample)
+    if ref is not None and su.check_out is not None:
+        result["parity"] = parity(su, ref)
     if result["cpu_baseline"]:
         # the GPU's throughput over the oracle's on all host threads (context: the oracle is a
         # plain fp64 reference, never tuned)
