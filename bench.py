@@ -101,8 +101,9 @@ def single_gpu_guard(args):
         sys.exit(2)
 
 
-def counters_traffic():
-    """HBM bytes per launch from the committed counter run, if the kernel is unchanged since."""
+def counters_traffic(field="traffic_bytes_per_dispatch"):
+    """A figure of the committed counter run (by default the HBM bytes per launch), if the kernel
+    is unchanged since."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     fields = {}
@@ -116,7 +117,7 @@ def counters_traffic():
     if fields.get("kernel_source_sha256") != h:
         return None
     try:
-        return float(fields["traffic_bytes_per_dispatch"])
+        return float(fields[field])
     except (KeyError, ValueError):
         return None
 
@@ -576,6 +577,10 @@ def main():
         "kernel_avg_us": launch_avg_ms * 1e3,
         "algorithmic_bytes_per_launch": su.launch_bytes,
     }
+    if default_launch:
+        # the share of the kernel's time the SIMDs spent issuing VALU instructions, from the same
+        # committed counter run (null once the kernel source has changed since)
+        result["valu_busy"] = counters_traffic("valu_busy_fraction")
     if len(su.sets) > 1 and not args.graph and not args.no_warm:
         # Context only, not the figure above: the same buffer set every launch, so the inputs
         # are served largely from the 256 MB Infinity Cache (warm).
