@@ -163,6 +163,26 @@ def device_forward_case(B, T, C, *, seed, k_sigma=1.0, device="cuda:0"):
     return dict(B=B, T=T, C=C, w=w, u=u, k=k, v=v)
 
 
+def device_timemix_case(B, T, C, *, seed, device="cuda:0"):
+    """Inputs for rwkv4_timemix_fused too large to draw on the host: fp16 x, k, v ~ N(0, 1)
+    drawn on the device as in device_forward_case (in that order, from one generator seeded with
+    `seed`); x_prev, the mixes, w and u on the host as in timemix_case."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    draw = lambda: torch.randn((B, T, C), generator=g, device=device,  # noqa: E731
+                               dtype=torch.float32).to(torch.float16)
+    x, k, v = draw(), draw(), draw()
+    h = rng_for(2, seed)
+    w, u = decay_bonus(C)
+    x_prev = _normal(h, (B, C), "f16")
+    mix_k = h.uniform(0.0, 1.0, C).astype(np.float32)
+    mix_v = h.uniform(0.0, 1.0, C).astype(np.float32)
+    mix_r = h.uniform(0.0, 1.0, C).astype(np.float32)
+    return dict(B=B, T=T, C=C, w=w, u=u, x=x, x_prev=x_prev, mix_k=mix_k, mix_v=mix_v, mix_r=mix_r,
+                k=k, v=v)
+
+
 def timemix_case(B, T, C, *, seed, in_dtype="f16", out_dtype=None, index=2, prior=False):
     """Inputs for rwkv4_timemix_fused.
     Draw order: x, x_prev, mix_k, mix_v, mix_r, k, v, [aa, bb, pp]."""
