@@ -7,7 +7,9 @@ first and last of the ragged last channel tile among them) are copied back: the 
 recurrence checks every output element of those channels and their final states, and its
 direct sums check 240 points among them (tile edges, the last tokens, tokens whose offsets
 pass 2^31).  Over the whole output: every element written and none past the end (canary),
-and for the ungated forward every y within [min v, max v] (a convex combination of values)."""
+and for the ungated forward every y within [min v, max v] (a convex combination of values).
+The decode step runs at B262144 C4104, whose state planes put the offsets of the last plane
+past 2^31; sampled lanes (the last ones among them) are checked against the oracle's step."""
 import numpy as np
 import pytest
 
@@ -109,3 +111,31 @@ def test_timemix_past_2_31_elements(algo, chunk):
     check_state(so[:, :, ci].double().cpu().numpy(), ref, f"huge time mix {algo}/{chunk}")
     assert np.array_equal(xl[:, ci].double().cpu().numpy(), ref["x_last"]), "x_last differs"
     del y, yfull, c
+
+
+def test_step_state_offsets_past_2_31():
+    import rwkv_wkv_linear_amd as rw
+    t = torch()
+    _cache.clear()
+    Bs = 262144
+    assert 2 * Bs * C > 2 ** 31
+    note(f"huge decode layer B{Bs} C{C} drawn on the device")
+    lay = wi.device_step_layer(Bs, C, seed=2026)
+    g = np.random.default_rng(2026)
+    lb = np.concatenate([[0, 0, Bs - 1, Bs - 1, Bs - 1], g.integers(0, Bs, 251)])
+    lc = np.concatenate([[0, C - 1, 0, C - 4, C - 1], g.integers(0, C, 251)])
+    bi, cj = t.from_numpy(lb).cuda(), t.from_numpy(lc).cuda()
+    pick = lambda a: a[bi, cj].double().cpu().numpy()[None]  # noqa: E731  [1, n] lanes as channels
+    sub = dict(B=1, C=lb.size, w=lay["w"][lc], u=lay["u"][lc], k=pick(lay["k"]), v=pick(lay["v"]),
+               r=pick(lay["r"]), state=np.stack([pick(lay["state"][q]) for q in range(3)]))
+    ref = oracle.step(sub)
+    y, yfull = poisoned((Bs, C), "f16")
+    note(f"huge decode step B{Bs} C{C}")
+    rw.rwkv4_wkv_step(lay["k"], lay["v"], lay["r"], t.from_numpy(lay["w"]).cuda(), t.from_numpy(lay["u"]).cuda(),
+                      lay["state"], y=y)
+    t.cuda.synchronize()
+    assert canary_ok(yfull, Bs * C), "write past the end of y"
+    assert not bool(t.isnan(y).any()), "an output element was not written"
+    check_output(pick(y), ref, TOL["f16"], "huge decode step: sampled lanes", argmax=False, out_dtype="f16")
+    check_state(np.stack([pick(lay["state"][q]) for q in range(3)]), ref, "huge decode step: sampled lanes")
+    del y, yfull, lay

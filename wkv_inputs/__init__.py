@@ -183,6 +183,21 @@ def device_timemix_case(B, T, C, *, seed, device="cuda:0"):
                 k=k, v=v)
 
 
+def device_step_layer(B, C, *, seed, device="cuda:0"):
+    """One decode layer too large to draw on the host: fp16 k, v, r ~ N(0, 1) and the state
+    (aa ~ N(0, 1), bb = |N(0, 1)|, pp ~ U(-5, 5), fp32), drawn on the device in that order from
+    one generator seeded with `seed`; w and u by the recipe above."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    n = lambda: torch.randn((B, C), generator=g, device=device, dtype=torch.float32)  # noqa: E731
+    k, v, r = n().to(torch.float16), n().to(torch.float16), n().to(torch.float16)
+    aa, bb = n(), n().abs_()
+    pp = torch.rand((B, C), generator=g, device=device, dtype=torch.float32).mul_(10.0).sub_(5.0)
+    w, u = decay_bonus(C)
+    return dict(B=B, C=C, w=w, u=u, k=k, v=v, r=r, state=torch.stack([aa, bb, pp]))
+
+
 def timemix_case(B, T, C, *, seed, in_dtype="f16", out_dtype=None, index=2, prior=False):
     """Inputs for rwkv4_timemix_fused.
     Draw order: x, x_prev, mix_k, mix_v, mix_r, k, v, [aa, bb, pp]."""
