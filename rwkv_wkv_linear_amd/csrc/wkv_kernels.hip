@@ -342,21 +342,30 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
     const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
     uint64_t w[MAXT][4];
     const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
+    // The words of every tile are requested before any is checked: with each tile's check next
+    // to its loads, the compiler waited for that tile's words before requesting the next
+    // tile's, one memory round trip per predecessor on every poll.  Only the cnt tiles in use
+    // are read (the polls share the memory channels with the publishes they wait for).
     auto read_all = [&]() -> bool {
-        bool all = true;
 #pragma unroll
         for (int m = 0; m < MAXT; ++m) {
             if (m < cnt) {
                 const uint64_t *src = tiles + m * (4 * kTileChannels) + ch;
-                const uint32_t want = (m == 0 && lo_incl) ? want_incl : want_agg;
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
+                for (int f = 0; f < 4; ++f)
                     w[m][f] = __hip_atomic_load(src + f * kTileChannels, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    all = all && (uint32_t)(w[m][f] >> 32) == want;
-                }
             }
         }
-        return __all(all);
+        uint32_t ok = 1u;
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+            const uint32_t want = (m == 0 && lo_incl) ? want_incl : want_agg;
+            uint32_t tm = 1u;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) tm &= (uint32_t)((uint32_t)(w[m][f] >> 32) == want);
+            ok &= tm | (uint32_t)(m >= cnt);
+        }
+        return __all(ok != 0u);
     };
     // one read site (a second inlined copy of read_all would hold a second set of words)
     bool failed = false;
