@@ -947,10 +947,11 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
     const float uc = cok ? u_raw : 0.f;
     float xs = 0.f, mr = 0.f, mk = 0.f, mv = 0.f;
     if constexpr (MODE == MODE_TIMEMIX) {
-        // wave 0: x[tile_t0 - 1] or x_prev (zeros if absent); later waves read it from LDS
-        const bool from_x = tile_t0 > 0, from_prev = tile_t0 == 0 && a.x_prev != nullptr;
+        // the token before the wave's first: x[t0 - 1], or x_prev (zeros if absent) at t0 = 0; a
+        // wave past T reads a valid address it does not use
+        const bool from_x = t0 > 0 && t0 <= a.T, from_prev = t0 == 0 && a.x_prev != nullptr;
         const TIn *xsrc = from_prev ? static_cast<const TIn *>(a.x_prev) + b * C + cs
-                                    : GR + (from_x ? (b * a.T + tile_t0 - 1) * C + cs : 0);
+                                    : GR + (from_x ? (b * a.T + t0 - 1) * C + cs : 0);
         const float xv = (float)*xsrc;
         const float mr_raw = a.mix_r[cs], mk_raw = a.mix_k[cs], mv_raw = a.mix_v[cs];
         xs = (from_x || from_prev) ? xv : 0.f;
@@ -1058,16 +1059,15 @@ __device__ __forceinline__ void tile_body(const ForwardArgs &a, const ChunkWorks
         publish(ws, chain + tt, kIncl, agg, lane, lp != 0);
     }
     if constexpr (NT == 3) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's gate rows have landed,
-        __syncthreads();                // and every other wave's (the time mix reads the previous wave's last x)
+        // this wave's gate rows have landed; the emit reads no other wave's (each wave loaded the
+        // token before its first itself), so a wave starts as soon as its own rows are in
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
     }
     const St st = combine(prefix, excl, (float)std::min<int64_t>((int64_t)wv * L, tile_len), wc);
 
     // Phase E: emit y for the wave's tokens, starting from st.
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (MODE == MODE_TIMEMIX) {
-        if (wv > 0) xs = (float)gr[-CW];  // the previous wave's last row
-    }
     const St fin = emit_wave<TIn, TOut, MODE, L>(a, st, Xs, fast, kmax, kr, vr, gr,
                                                  rows + ((size_t)0 * TW + wv * L) * CW,
                                                  rows + ((size_t)1 * TW + wv * L) * CW, wc, uc, ew, eu, ga, gb,
