@@ -340,7 +340,7 @@ __device__ St fold_published(const ChunkWorkspace &ws, int64_t chain, int64_t lo
                              float wc, float TW, int ch) {
     const int cnt = (int)(hi - lo);
     const uint32_t want_agg = (ws.epoch << 2) | kAgg, want_incl = (ws.epoch << 2) | kIncl;
-    uint64_t w[MAXT][4];
+    uint64_t w[MAXT][4] = {};  // slots past cnt are never loaded; their checks are masked
     const uint64_t *tiles = ws.words + (chain + lo) * (4 * kTileChannels);  // wave-uniform
     // The words of every tile are requested before any is checked: with each tile's check next
     // to its loads, the compiler waited for that tile's words before requesting the next
