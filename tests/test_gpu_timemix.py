@@ -83,6 +83,24 @@ def test_fp32_odd_channels_no_prev(algo, chunk):
     check_all(out, ref, nop, f"timemix fp32 C=37 {algo}/{chunk}", True)
 
 
+@pytest.mark.parametrize("T", [80, 129, 160, 250, 272])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("chunked", 64), ("chunked", 128), ("two_pass", 128)])
+@pytest.mark.parametrize("with_prev", [True, False])
+def test_wave_boundaries(T, algo, chunk, with_prev):
+    # Every wave of a tile takes the token before its first (the token shift) itself: from x at
+    # t0 - 1, from x_prev at t0 = 0.  These lengths put a wave's first token exactly at T (80 with
+    # 16-token waves, 160 with 32-token waves), give a tile's first wave a single token (129),
+    # and end on a partial wave after full ones (250, 272), on ragged channels (C = 136).
+    case = wi.timemix_case(2, T, 136, seed=64 + T, prior=True)
+    if not with_prev:
+        case = dict(case, x_prev=np.zeros_like(case["x_prev"]))
+    key = ("waves", T, with_prev)
+    if key not in _cache:
+        _cache[key] = oracle.timemix(case)
+    out = run(case, algo, chunk, with_prev=with_prev, label=f"wave boundaries T={T}")
+    check_all(out, _cache[key], case, f"timemix T={T} {algo}/{chunk} prev={with_prev}", False)
+
+
 def test_zero_tokens():
     import rwkv_wkv_linear_amd as rw
     t = torch()
